@@ -1,0 +1,172 @@
+/*
+ * libtv -- token-tree verification on AMD MI355X (gfx950).  C ABI.
+ *
+ * The verification step of draft-then-verify speculative decoding: the
+ * target model scores a whole draft tree in one forward pass under a tree
+ * attention mask, then an accept/reject walk decides which draft tokens are
+ * kept and draws one extra token.
+ *
+ * Conventions shared by every call
+ *  - All array pointers are DEVICE pointers unless stated otherwise.  The
+ *    caller owns every buffer; the library never allocates, frees or
+ *    synchronises.  Scratch space comes from the caller's `workspace`.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on it and returns.
+ *  - bf16 tensors are passed as uint16_t bit patterns (IEEE binary32 with the
+ *    low 16 mantissa bits dropped).
+ *  - Scalar and shape arguments are checked on the host before anything is
+ *    enqueued; a failed check returns a negative tv_status and enqueues
+ *    nothing.  A failed launch returns TV_ERR_HIP.
+ *  - Tree conventions: nodes 0..N-1 of each sequence; node 0 is the root (the
+ *    last committed token) with parent -1; parent[i] < i for i >= 1;
+ *    children of a node are taken in increasing index order.
+ *  - Calls are stateless and deterministic for fixed inputs and seed.  Calls
+ *    on different streams must not share a workspace.
+ *
+ * Sources: the pages this library follows are cited per call by page and
+ * section: the EAGLE explainer (0h-n0.github.io/posts/paper-2401-10774) and
+ * the speculative-decoding survey explainer
+ * (0h-n0.github.io/posts/paper-2401-07851).
+ */
+#ifndef TV_H_
+#define TV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TV_OK = 0,
+    TV_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad temperature, ... */
+    TV_ERR_UNSUPPORTED = -2, /* valid but not implemented here: N > 64, D != 128 */
+    TV_ERR_BAD_TREE = -3,    /* parent[] violates the tree conventions (per-sequence status) */
+    TV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query says */
+    TV_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} tv_status;
+
+/* Largest tree (nodes including the root) handled: one 64-bit ancestor word per node. */
+#define TV_MAX_NODES 64
+/* Head dimension handled by the attention kernels. */
+#define TV_HEAD_DIM 128
+
+/* Human-readable text for a tv_status value (static storage, never NULL). */
+const char* tv_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int tv_version(void);
+
+/*
+ * tv_build_tree_mask -- ancestor bitsets of a draft tree.
+ *
+ * EAGLE explainer, section on parallel verification with a static tree: one
+ * target pass with a tree attention mask verifies every root-to-node path, so
+ * node i may see exactly its ancestors and itself.
+ *
+ *   parent     int32 [B,N]   parent index of each node (root: -1).
+ *   anc_mask   uint64 [B,N]  out: bit j set iff node j is i or an ancestor of i.
+ *   depth      int32 [B,N]   out: depth of each node (root 0); callers derive
+ *                            rotary positions as L + depth.
+ *   seq_status int32 [B]     out, may be NULL: 0, or TV_ERR_BAD_TREE when the
+ *                            sequence's parent[] is invalid; such a sequence
+ *                            gets anc_mask 0 and depth -1 throughout.
+ * Sizes: B >= 0 (B == 0 is a no-op), 1 <= N <= TV_MAX_NODES.
+ */
+int tv_build_tree_mask(const int32_t* parent, int B, int N, uint64_t* anc_mask, int32_t* depth,
+                       int32_t* seq_status, void* stream);
+
+/*
+ * tv_tree_attention -- ancestor-masked attention of every tree node over the
+ * committed KV cache plus its own root-to-node path.
+ *
+ * EAGLE explainer, section on parallel verification with a static tree (tree
+ * attention mask); survey explainer, formal definition, verification phase
+ * (the target distribution at draft position i conditions on the context and
+ * the drafts before it).
+ *
+ * For sequence b, query head h (KV head g = h / (Hq/Hkv)) and node i:
+ *   out[b,i,h] = sum_j softmax_j(scale * Q[b,i,h] . k_j) v_j over
+ *   j in { K_cache[b,g,0..L-1] } and { K_tree[b,j,g] : j ancestor-or-self of i }.
+ *
+ *   Q        bf16 [B,N,Hq,D]      queries (rotary encoding already applied).
+ *   K_cache  bf16 [B,Hkv,L,D]     committed keys, head-major (may be NULL if L == 0).
+ *   V_cache  bf16 [B,Hkv,L,D]     committed values (may be NULL if L == 0).
+ *   K_tree   bf16 [B,N,Hkv,D]     keys of the tree nodes.
+ *   V_tree   bf16 [B,N,Hkv,D]     values of the tree nodes.
+ *   anc_mask uint64 [B,N]         from tv_build_tree_mask; must describe a valid tree.
+ *   out      fp32 [B,N,Hq,D]      out.
+ *   scale    softmax scale, conventionally 1/sqrt(D); must be finite.
+ * Sizes: B >= 0, 1 <= N <= TV_MAX_NODES, Hq >= Hkv >= 1 with Hq % Hkv == 0,
+ * D == TV_HEAD_DIM, L >= 0.
+ * Numerics: QK^T in bf16 with fp32 accumulation, softmax in fp32, P.V with
+ * P and V in fp16 and fp32 accumulation.  Precondition: |V| <= 65504.
+ * Workspace: at least tv_tree_attention_workspace(...) bytes, 256-byte aligned
+ * (may be NULL when that size is 0).
+ */
+size_t tv_tree_attention_workspace(int B, int N, int Hq, int Hkv, int D, int L);
+int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t* V_cache,
+                      const uint16_t* K_tree, const uint16_t* V_tree, const uint64_t* anc_mask,
+                      float* out, int B, int N, int Hq, int Hkv, int D, int L, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tv_spec_accept -- accept/reject walk over the tree (greedy or lossless
+ * speculative sampling).
+ *
+ * Survey explainer, formal definition, accept/reject phase: a draft x drawn
+ * from the draft distribution p is accepted if r < min(1, q(x)/p(x)),
+ * r ~ U[0,1]; at the first rejection a token is drawn from
+ * norm(max(0, q - p)); the verification phase provides K+1 target
+ * distributions so that one extra token is always emitted.  Same page,
+ * classification of verification methods: greedy verification keeps drafts
+ * that equal the target's greedy choice; token-tree verification checks
+ * all candidate paths at once and stays lossless.
+ *
+ *   q_logits     fp32 [B,N,V]  row u = target logits at tree position u (they
+ *                              predict u's children; row u is u's bonus row).
+ *   p_logits     fp32 [B,N,V]  row c = draft logits that produced node c (row 0
+ *                              unused).  May be NULL when greedy.
+ *   draft_tokens int32 [B,N]   token of node c (entry 0 ignored); each in [0,V).
+ *   parent       int32 [B,N]   the tree; must be valid (see tv_build_tree_mask).
+ *   philox_seed  key of the Philox-4x32-10 uniforms: the accept test of node c
+ *                in sequence b uses counter (c, b, 0, 0), the final draw after
+ *                stopping at node u uses (u, b, 1, 0); U = (word0 >> 8) * 2^-24.
+ *   temperature  > 0 and finite in sampling mode (logits are divided by it);
+ *                ignored when greedy.
+ *   greedy       nonzero: keep the deepest path whose every draft equals the
+ *                argmax of its parent's target row (ties: smallest token, then
+ *                smallest end node); extra token = argmax of the end node's row.
+ *                zero: children of the current node are tested in index order;
+ *                each rejection replaces the target by norm(max(0, R - P_c));
+ *                if all children are rejected the extra token is drawn from the
+ *                residual, at a leaf from the leaf's own target row.
+ *   accept_len     int32 [B]   out: accepted draft nodes.
+ *   accepted_nodes int32 [B,N] out: their node indices root-to-leaf, -1 padded.
+ *   out_tokens     int32 [B,N] out: accepted tokens then the extra token, -1 padded.
+ * Sizes: B >= 0, 1 <= N <= TV_MAX_NODES, V >= 1.  Logits must be finite.
+ * Workspace: at least tv_spec_accept_workspace(B,N,V,greedy) bytes, 256-byte
+ * aligned.
+ */
+size_t tv_spec_accept_workspace(int B, int N, int V, int greedy);
+int tv_spec_accept(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
+                   const int32_t* parent, int B, int N, int V, uint64_t philox_seed, float temperature,
+                   int greedy, int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tv_philox_uniforms -- the uniforms tv_spec_accept draws, for auditing.
+ *
+ *   triples  uint32 [n,3]  (node, sequence, purpose) counters, device memory.
+ *   out_u    fp32 [n]      out: U(seed, node, sequence, purpose), may be NULL.
+ *   out_raw  uint32 [n,4]  out: the raw Philox-4x32-10 block, may be NULL.
+ */
+int tv_philox_uniforms(uint64_t seed, const uint32_t* triples, int n, float* out_u, uint32_t* out_raw,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_H_ */

@@ -1,0 +1,289 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bars: tree mask, greedy walk and Philox bit-exact; attention max abs error
+<= 1e-2 and relative L2 <= 1e-3 against the fp64 oracle; sampling walk
+bit-exact on every sequence whose oracle walk records no near-boundary
+decision, with flagged flips below 0.01% of draft nodes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, Workload, accept_inputs, attention_inputs, bf16_to_f64, chain, random_tree, \
+    static_tree_60, tiny_workloads
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+RTOL_L2 = 1e-3
+FLIP_RATE = 1e-4
+
+
+@pytest.fixture(scope="module")
+def tv():
+    import token_tree_verification_amd as m
+    m.library()
+    return m
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _attn_check(got, ref, what):
+    err = np.abs(got - ref).max()
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert np.isfinite(got).all(), what
+    assert err <= ATOL and rel <= RTOL_L2, f"{what}: max abs {err:.3g}, rel L2 {rel:.3g}"
+    return err, rel
+
+
+# ------------------------------------------------------------------ philox --
+def test_philox_bit_exact(tv):
+    rng = np.random.default_rng(1)
+    n = 1 << 20
+    tri = np.stack([rng.integers(0, 64, n), rng.integers(0, 4096, n), rng.integers(0, 3, n)], 1).astype(np.int32)
+    tri[: 3 * 1000] = np.stack([np.arange(3000) % 64, np.arange(3000) // 64, np.arange(3000) % 3], 1)
+    for seed in (0, 1, 0x123456789ABCDEF, 2 ** 64 - 1):
+        u, raw = tv.philox_uniforms(seed, torch.from_numpy(tri).to(dev()))
+        key = np.array([[seed & 0xFFFFFFFF, seed >> 32]] * n, np.uint32)
+        ctr = np.concatenate([tri.astype(np.uint32), np.zeros((n, 1), np.uint32)], 1)
+        want = oracle.philox4x32_10(ctr, key)
+        assert np.array_equal(_np(raw).view(np.uint32), want)
+        wu = oracle.uniforms(seed, tri.astype(np.uint32))
+        assert np.array_equal(_np(u).astype(np.float64), wu)
+
+
+# -------------------------------------------------------------- tree mask --
+@pytest.mark.parametrize("N", [1, 2, 6, 17, 33, 60, 64])
+def test_tree_mask_bit_exact(tv, N):
+    B = 48
+    par = np.stack([random_tree(N, 1 + b % 9, 500 + b) for b in range(B)]).astype(np.int32)
+    if N == 60:
+        par[0] = static_tree_60()
+    if N > 1:
+        par[1] = chain(N)
+        par[2, N - 1] = N - 1      # self-parent
+        par[3, 0] = 0              # root with a parent
+        par[4, 1] = -1             # second root
+        par[5, N - 1] = -7
+    anc, depth, status = tv.build_tree_mask(torch.from_numpy(par).to(dev()))
+    o_anc, o_depth, o_status = oracle.tree_mask(par)
+    assert np.array_equal(_np(anc).view(np.uint64), o_anc[:, :, 0])
+    assert np.array_equal(_np(depth), o_depth)
+    assert np.array_equal(_np(status), o_status)
+
+
+def test_tree_mask_empty_batch(tv):
+    anc, depth, status = tv.build_tree_mask(torch.zeros((0, 5), dtype=torch.int32, device=dev()))
+    assert anc.shape == (0, 5)
+
+
+# -------------------------------------------------------------- attention --
+def _run_attention(tv, w, parent=None, L=None, seed=None):
+    par = w.parents() if parent is None else parent
+    Q, Kc, Vc, Kt, Vt = attention_inputs(w, device=dev(), seed=seed, L=L)
+    anc, _, _ = tv.build_tree_mask(torch.from_numpy(par.astype(np.int32)).to(dev()))
+    out = tv.tree_attention(Q, Kc, Vc, Kt, Vt, anc)
+    torch.cuda.synchronize()
+    return (Q, Kc, Vc, Kt, Vt), par, out
+
+
+@pytest.mark.parametrize("w", tiny_workloads(), ids=lambda w: w.name)
+def test_attention_tiny_full_compare(tv, w):
+    (Q, Kc, Vc, Kt, Vt), par, out = _run_attention(tv, w)
+    ref = oracle.tree_attention(*(bf16_to_f64(t) for t in (Q, Kc, Vc, Kt, Vt)), par)
+    _attn_check(_np(out).astype(np.float64), ref, w.name)
+
+
+# shapes hitting each row packing (R = G*N <= 32, <= 64, > 64), ragged key tails,
+# single-key caches and splits
+@pytest.mark.parametrize("B,N,Hq,Hkv,L,tree", [
+    (1, 1, 1, 1, 1, "chain"),
+    (2, 1, 8, 8, 0, "chain"),
+    (3, 5, 6, 2, 31, "random"),
+    (2, 13, 4, 1, 33, "random"),
+    (1, 32, 1, 1, 64, "random"),
+    (2, 33, 2, 2, 95, "random"),
+    (1, 64, 3, 1, 513, "random"),
+    (2, 7, 16, 1, 200, "random"),
+    (1, 64, 8, 8, 1, "random"),
+    (1, 40, 2, 2, 4097, "random"),
+])
+def test_attention_shapes(tv, B, N, Hq, Hkv, L, tree):
+    w = Workload("shape", B=B, N=N, Hq=Hq, Hkv=Hkv, D=128, L=L, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),
+                 tree=tree, max_depth=6, data_seed=B * 1000 + N * 10 + L)
+    (Q, Kc, Vc, Kt, Vt), par, out = _run_attention(tv, w)
+    ref = oracle.tree_attention(*(bf16_to_f64(t) for t in (Q, Kc, Vc, Kt, Vt)), par)
+    _attn_check(_np(out).astype(np.float64), ref, f"B{B} N{N} Hq{Hq} Hkv{Hkv} L{L}")
+
+
+def test_attention_zero_query_is_mean_of_visible_values(tv):
+    w = Workload("zq", B=2, N=20, Hq=4, Hkv=2, D=128, L=300, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),
+                 tree="random", max_depth=5, data_seed=77)
+    par = w.parents()
+    Q, Kc, Vc, Kt, Vt = attention_inputs(w, device=dev())
+    Q.zero_()
+    anc, _, _ = tv.build_tree_mask(torch.from_numpy(par.astype(np.int32)).to(dev()))
+    out = _np(tv.tree_attention(Q, Kc, Vc, Kt, Vt, anc)).astype(np.float64)
+    vc, vt = bf16_to_f64(Vc), bf16_to_f64(Vt)
+    for b in range(2):
+        anc_sets = oracle.ancestor_sets(par[b])
+        for i in range(20):
+            for h in range(4):
+                rows = np.concatenate([vc[b, h // 2], vt[b, sorted(anc_sets[i]), h // 2]])
+                assert np.abs(out[b, i, h] - rows.mean(0)).max() < 2e-3
+
+
+def test_attention_deterministic(tv):
+    w = CONFIGS["c2"]
+    (Q, Kc, Vc, Kt, Vt), par, out1 = _run_attention(tv, w)
+    anc, _, _ = tv.build_tree_mask(torch.from_numpy(par.astype(np.int32)).to(dev()))
+    out2 = tv.tree_attention(Q, Kc, Vc, Kt, Vt, anc)
+    assert torch.equal(out1, out2)
+
+
+def _sample_heads(w, k, seed):
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (w.B - 1, w.Hq - 1)}
+    while len(pairs) < k:
+        pairs.add((int(rng.integers(0, w.B)), int(rng.integers(0, w.Hq))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_attention_full_config_sampled(tv, name):
+    """Full-size inputs in the benchmark's launch configuration; the oracle
+    recomputes sampled (sequence, head) slices exactly."""
+    w = CONFIGS[name]
+    (Q, Kc, Vc, Kt, Vt), par, out = _run_attention(tv, w)
+    G = w.G
+    for b, h in _sample_heads(w, 6, 3):
+        g = h // G
+        sl = lambda t, s: bf16_to_f64(t[b:b + 1, s]) if s is not None else bf16_to_f64(t[b:b + 1])
+        ref = oracle.tree_attention(bf16_to_f64(Q[b:b + 1, :, h:h + 1]), bf16_to_f64(Kc[b:b + 1, g:g + 1]),
+                                    bf16_to_f64(Vc[b:b + 1, g:g + 1]), bf16_to_f64(Kt[b:b + 1, :, g:g + 1]),
+                                    bf16_to_f64(Vt[b:b + 1, :, g:g + 1]), par[b:b + 1])
+        got = _np(out[b:b + 1, :, h:h + 1]).astype(np.float64)
+        _attn_check(got, ref, f"{name} b={b} h={h}")
+
+
+# ----------------------------------------------------------------- accept --
+def _accept_gpu(tv, q, p, draft, parent_t, seed, T, greedy):
+    a, n, t = tv.spec_accept(q, p, draft, parent_t, seed=seed, temperature=T, greedy=greedy)
+    torch.cuda.synchronize()
+    return _np(a), _np(n), _np(t)
+
+
+def _compare_walk(gpu, ref, greedy):
+    a, n, t = gpu
+    same = (a == ref["accept_len"]) & (n == ref["accepted_nodes"]).all(1) & (t == ref["out_tokens"]).all(1)
+    if greedy:
+        assert same.all(), f"greedy mismatch in sequences {np.nonzero(~same)[0].tolist()}"
+        return 0
+    flagged = ref["flags"] > 0
+    bad = ~same & ~flagged
+    assert not bad.any(), f"unflagged sampling mismatch in sequences {np.nonzero(bad)[0].tolist()}"
+    return int((~same & flagged).sum())
+
+
+@pytest.mark.parametrize("w", tiny_workloads(), ids=lambda w: w.name)
+def test_accept_tiny(tv, w):
+    q, p, draft, parent_t = accept_inputs(w, device=dev())
+    qn, pn, dn, parn = _np(q), _np(p), _np(draft), _np(parent_t)
+    for T in w.temperatures:
+        greedy = T == 0.0
+        for seed in range(20):
+            gpu = _accept_gpu(tv, q, None if greedy else p, draft, parent_t, seed, T if not greedy else 1.0, greedy)
+            ref = oracle.spec_accept(qn, None if greedy else pn, dn, parn, seed=seed, temperature=T or 1.0,
+                                     greedy=greedy)
+            _compare_walk(gpu, ref, greedy)
+            if greedy:
+                break
+
+
+def test_accept_sampling_with_uniform_drafts(tv):
+    """Drafts drawn uniformly (many rejections and deep residual chains)."""
+    rng = np.random.default_rng(4)
+    B, N, V = 16, 40, 301  # V % 4 != 0 exercises the scalar load path
+    q = rng.normal(scale=2.0, size=(B, N, V)).astype(np.float32)
+    p = rng.normal(scale=2.0, size=(B, N, V)).astype(np.float32)
+    draft = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    par = np.stack([random_tree(N, 3, 50 + b) for b in range(B)]).astype(np.int32)
+    tq, tp, td, tpar = (torch.from_numpy(x).to(dev()) for x in (q, p, draft, par))
+    flips = 0
+    for seed in range(30):
+        for T in (1.0, 0.6):
+            gpu = _accept_gpu(tv, tq, tp, td, tpar, seed, T, False)
+            ref = oracle.spec_accept(q, p, draft, par, seed=seed, temperature=T)
+            flips += _compare_walk(gpu, ref, False)
+    assert flips <= FLIP_RATE * 60 * B * (N - 1)
+
+
+def test_accept_edge_cases(tv):
+    rng = np.random.default_rng(8)
+    # root only: extra token from the root row; V = 1; invalid tree
+    for N, V in ((1, 50), (3, 1), (5, 7)):
+        q = rng.normal(size=(2, N, V)).astype(np.float32)
+        p = rng.normal(size=(2, N, V)).astype(np.float32)
+        draft = rng.integers(0, V, size=(2, N)).astype(np.int32)
+        par = np.tile(chain(N), (2, 1)).astype(np.int32)
+        tq, tp, td, tpar = (torch.from_numpy(x).to(dev()) for x in (q, p, draft, par))
+        for greedy in (True, False):
+            for seed in range(5):
+                gpu = _accept_gpu(tv, tq, tp, td, tpar, seed, 0.9, greedy)
+                ref = oracle.spec_accept(q, p, draft, par, seed=seed, temperature=0.9, greedy=greedy)
+                _compare_walk(gpu, ref, greedy)
+    bad = np.array([[-1, 0, 0], [-1, 2, 0]], np.int32)
+    q = torch.zeros((2, 3, 10), device=dev())
+    a, n, t = tv.spec_accept(q, q, torch.zeros((2, 3), dtype=torch.int32, device=dev()),
+                             torch.from_numpy(bad).to(dev()), seed=0, temperature=1.0)
+    assert _np(a).tolist()[1] == -1 and (_np(t)[1] == -1).all() and _np(a)[0] >= 0
+    a, n, t = tv.spec_accept(torch.zeros((0, 3, 10), device=dev()), None,
+                             torch.zeros((0, 3), dtype=torch.int32, device=dev()),
+                             torch.zeros((0, 3), dtype=torch.int32, device=dev()), greedy=True)
+    assert a.numel() == 0
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_accept_full_config(tv, name):
+    w = CONFIGS[name]
+    q, p, draft, parent_t = accept_inputs(w, device=dev())
+    qn, dn, parn = _np(q), _np(draft), _np(parent_t)
+    pn = _np(p)
+    flips, nodes = 0, 0
+    for T in w.temperatures + ((0.0,) if 0.0 not in w.temperatures else ()):
+        greedy = T == 0.0
+        seeds = [0] if greedy else list(range(4 if w.B * w.V > 10 ** 7 else 16))
+        for seed in seeds:
+            gpu = _accept_gpu(tv, q, None if greedy else p, draft, parent_t, seed, T or 1.0, greedy)
+            ref = oracle.spec_accept(qn, None if greedy else pn, dn, parn, seed=seed, temperature=T or 1.0,
+                                     greedy=greedy)
+            flips += _compare_walk(gpu, ref, greedy)
+            nodes += w.B * (w.N - 1)
+    assert flips <= FLIP_RATE * nodes
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_accept_sampling_seed_sweep(tv, name):
+    """Many Philox seeds on a full-size configuration: the flagged-flip rate
+    must stay below 0.01% of draft nodes."""
+    w = CONFIGS[name]
+    T = [t for t in w.temperatures if t > 0][0]
+    q, p, draft, parent_t = accept_inputs(w, device=dev())
+    qn, pn, dn, parn = _np(q), _np(p), _np(draft), _np(parent_t)
+    nseeds = {"c1": 400, "c2": 400, "c3": 60}[name]
+    flips = 0
+    for seed in range(nseeds):
+        gpu = _accept_gpu(tv, q, p, draft, parent_t, seed, T, False)
+        ref = oracle.spec_accept(qn, pn, dn, parn, seed=seed, temperature=T)
+        flips += _compare_walk(gpu, ref, False)
+    nodes = nseeds * w.B * (w.N - 1)
+    assert flips <= FLIP_RATE * nodes

@@ -1,0 +1,202 @@
+"""ctypes binding of libtv.so: argument checking and marshalling only.
+
+Every step of the verification path runs in the HIP kernels behind the C ABI
+declared in include/tv.h; this module checks tensor shapes, dtypes and
+devices, allocates outputs and workspaces with torch (device memory only),
+and passes raw pointers plus the current HIP stream.  There is no CPU
+fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtv.so")
+
+TV_OK = 0
+_lib = None
+
+
+class TVError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        msg = _load().tv_status_string(status).decode()
+        super().__init__(f"{func} failed with status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libtv.so is not built ({LIB_PATH}); run __graft_entry__.build() "
+                           "or python token_tree_verification_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, U64, SZ, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_float
+    lib.tv_status_string.argtypes = [I]
+    lib.tv_status_string.restype = ctypes.c_char_p
+    lib.tv_version.argtypes = []
+    lib.tv_version.restype = I
+    lib.tv_build_tree_mask.argtypes = [P, I, I, P, P, P, P]
+    lib.tv_build_tree_mask.restype = I
+    lib.tv_tree_attention_workspace.argtypes = [I, I, I, I, I, I]
+    lib.tv_tree_attention_workspace.restype = SZ
+    lib.tv_tree_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P]
+    lib.tv_tree_attention.restype = I
+    lib.tv_spec_accept_workspace.argtypes = [I, I, I, I]
+    lib.tv_spec_accept_workspace.restype = SZ
+    lib.tv_spec_accept.argtypes = [P, P, P, P, I, I, I, U64, F, I, P, P, P, P, SZ, P]
+    lib.tv_spec_accept.restype = I
+    lib.tv_philox_uniforms.argtypes = [U64, P, I, P, P, P]
+    lib.tv_philox_uniforms.restype = I
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes handle of libtv.so (raises if it is not built)."""
+    return _load()
+
+
+def _check(func, status):
+    if status != TV_OK:
+        raise TVError(func, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.device != device or workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace must hold {nbytes} bytes on {device}")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def build_tree_mask(parent: torch.Tensor):
+    """parent int32 [B,N] -> (anc_mask int64 [B,N] holding the uint64 bitsets,
+    depth int32 [B,N], seq_status int32 [B])."""
+    _need(parent, "parent", torch.int32, 2)
+    B, N = parent.shape
+    dev = parent.device
+    anc = torch.empty((B, N), dtype=torch.int64, device=dev)
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check("tv_build_tree_mask",
+           _load().tv_build_tree_mask(_ptr(parent), B, N, _ptr(anc), _ptr(depth), _ptr(status), _stream(dev)))
+    return anc, depth, status
+
+
+def attention_workspace_bytes(B, N, Hq, Hkv, D, L) -> int:
+    return int(_load().tv_tree_attention_workspace(B, N, Hq, Hkv, D, L))
+
+
+def tree_attention(Q, K_cache, V_cache, K_tree, V_tree, anc_mask, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Q bf16 [B,N,Hq,D]; K/V_cache bf16 [B,Hkv,L,D]; K/V_tree bf16 [B,N,Hkv,D];
+    anc_mask int64 [B,N] -> out fp32 [B,N,Hq,D]."""
+    _need(Q, "Q", torch.bfloat16, 4)
+    dev = Q.device
+    B, N, Hq, D = Q.shape
+    for name, t in (("K_cache", K_cache), ("V_cache", V_cache), ("K_tree", K_tree), ("V_tree", V_tree)):
+        _need(t, name, torch.bfloat16, 4, dev)
+    _need(anc_mask, "anc_mask", torch.int64, 2, dev)
+    Hkv, L = K_cache.shape[1], K_cache.shape[2]
+    if tuple(K_cache.shape) != (B, Hkv, L, D) or tuple(V_cache.shape) != (B, Hkv, L, D):
+        raise ValueError("K_cache/V_cache must be [B,Hkv,L,D]")
+    if tuple(K_tree.shape) != (B, N, Hkv, D) or tuple(V_tree.shape) != (B, N, Hkv, D):
+        raise ValueError("K_tree/V_tree must be [B,N,Hkv,D]")
+    if tuple(anc_mask.shape) != (B, N):
+        raise ValueError("anc_mask must be [B,N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, 4, dev)
+        if tuple(out.shape) != (B, N, Hq, D):
+            raise ValueError("out must be [B,N,Hq,D]")
+    ws = _workspace(attention_workspace_bytes(B, N, Hq, Hkv, D, L), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("tv_tree_attention",
+           _load().tv_tree_attention(_ptr(Q), _ptr(K_cache), _ptr(V_cache), _ptr(K_tree), _ptr(V_tree),
+                                     _ptr(anc_mask), _ptr(out), B, N, Hq, Hkv, D, L, float(scale), _ptr(ws), nbytes,
+                                     _stream(dev)))
+    return out
+
+
+def accept_workspace_bytes(B, N, V, greedy) -> int:
+    return int(_load().tv_spec_accept_workspace(B, N, V, int(bool(greedy))))
+
+
+def spec_accept(q_logits, p_logits, draft_tokens, parent, seed: int = 0, temperature: float = 1.0,
+                greedy: bool = False, workspace: Optional[torch.Tensor] = None, outputs=None):
+    """q_logits/p_logits fp32 [B,N,V] (p may be None when greedy); draft_tokens,
+    parent int32 [B,N] -> (accept_len int32 [B], accepted_nodes int32 [B,N],
+    out_tokens int32 [B,N])."""
+    _need(q_logits, "q_logits", torch.float32, 3)
+    dev = q_logits.device
+    B, N, V = q_logits.shape
+    if not greedy or p_logits is not None:
+        _need(p_logits, "p_logits", torch.float32, 3, dev)
+        if tuple(p_logits.shape) != (B, N, V):
+            raise ValueError("p_logits must be [B,N,V]")
+    _need(draft_tokens, "draft_tokens", torch.int32, 2, dev)
+    _need(parent, "parent", torch.int32, 2, dev)
+    if tuple(draft_tokens.shape) != (B, N) or tuple(parent.shape) != (B, N):
+        raise ValueError("draft_tokens and parent must be [B,N]")
+    if outputs is None:
+        acc_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        acc_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+        toks = torch.empty((B, N), dtype=torch.int32, device=dev)
+    else:
+        acc_len, acc_nodes, toks = outputs
+    ws = _workspace(accept_workspace_bytes(B, N, V, greedy), dev, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("tv_spec_accept",
+           _load().tv_spec_accept(_ptr(q_logits), _ptr(p_logits), _ptr(draft_tokens), _ptr(parent), B, N, V,
+                                  int(seed) & 0xFFFFFFFFFFFFFFFF, float(temperature), int(bool(greedy)),
+                                  _ptr(acc_len), _ptr(acc_nodes), _ptr(toks), _ptr(ws), nbytes, _stream(dev)))
+    return acc_len, acc_nodes, toks
+
+
+def philox_uniforms(seed: int, triples: torch.Tensor):
+    """triples int32 [n,3] (node, sequence, purpose) on the device ->
+    (uniforms fp32 [n], raw Philox blocks int32 [n,4] holding uint32 bits)."""
+    _need(triples, "triples", torch.int32, 2)
+    n = triples.shape[0]
+    dev = triples.device
+    u = torch.empty((n,), dtype=torch.float32, device=dev)
+    raw = torch.empty((n, 4), dtype=torch.int32, device=dev)
+    _check("tv_philox_uniforms",
+           _load().tv_philox_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(triples), n, _ptr(u), _ptr(raw),
+                                      _stream(dev)))
+    return u, raw
