@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of one token-tree verification step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+tree mask -> ancestor-masked tree attention -> accept/reject walk.  The
+headline workload is "batch 1 linear chain K=5, GQA 32/8 x 128, KV 4096,
+vocab 128256" with temperature-1.0 sampling; the greedy step is reported
+beside it.  Inputs are resident in HBM before timing starts and rotate over
+enough copies to exceed the 256 MB Infinity Cache.
+
+Prints ONE JSON line (rank 0) with the throughput (verified tree-nodes/s),
+the roofline of the dominant call measured live with HIP events on its
+stream, and the CPU oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified tree-nodes/sec + achieved HBM GB/s & MFMA util vs MI355X peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--temperature", type=float, default=None, help="sampling temperature (default: the config's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
+    return ap.parse_args()
+
+
+class Step:
+    """Pre-marshalled C-ABI calls of one verification step on one input copy."""
+
+    def __init__(self, tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, greedy, temperature, seed, dev):
+        import torch
+        self.lib = tv.library()
+        B, N, Hq, Hkv, D, L, V = w.B, w.N, w.Hq, w.Hkv, w.D, w.L, w.V
+        self.keep = [Q, Kc, Vc, Kt, Vt, q, p, draft, parent]
+        self.anc = torch.empty((B, N), dtype=torch.int64, device=dev)
+        self.depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.status = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, N, Hq, D), dtype=torch.float32, device=dev)
+        self.acc_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.acc_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.toks = torch.empty((B, N), dtype=torch.int32, device=dev)
+        aw = tv.attention_workspace_bytes(B, N, Hq, Hkv, D, L)
+        self.attn_ws = torch.zeros(max(aw, 256), dtype=torch.uint8, device=dev)
+        cw = tv.accept_workspace_bytes(B, N, V, greedy)
+        self.acc_ws = torch.zeros(max(cw, 256), dtype=torch.uint8, device=dev)
+        P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        self.mask_args = (P(parent), B, N, P(self.anc), P(self.depth), P(self.status), self.stream)
+        self.attn_args = (P(Q), P(Kc), P(Vc), P(Kt), P(Vt), P(self.anc), P(self.out), B, N, Hq, Hkv, D, L,
+                          ctypes.c_float(1.0 / math.sqrt(D)), P(self.attn_ws), ctypes.c_size_t(aw), self.stream)
+        self.acc_args = (P(q), None if greedy else P(p), P(draft), P(parent), B, N, V, ctypes.c_uint64(seed),
+                         ctypes.c_float(temperature), int(greedy), P(self.acc_len), P(self.acc_nodes), P(self.toks),
+                         P(self.acc_ws), ctypes.c_size_t(cw), self.stream)
+
+    def mask(self):
+        rc = self.lib.tv_build_tree_mask(*self.mask_args)
+        if rc:
+            raise RuntimeError(f"tv_build_tree_mask: {rc}")
+
+    def attention(self):
+        rc = self.lib.tv_tree_attention(*self.attn_args)
+        if rc:
+            raise RuntimeError(f"tv_tree_attention: {rc}")
+
+    def accept(self):
+        rc = self.lib.tv_spec_accept(*self.acc_args)
+        if rc:
+            raise RuntimeError(f"tv_spec_accept: {rc}")
+
+    def run(self):
+        self.mask()
+        self.attention()
+        self.accept()
+
+
+def attention_bytes(w):
+    kv = 2 * w.B * w.Hkv * w.L * w.D * 2
+    return kv + w.B * w.N * w.Hq * w.D * 2 + 2 * w.B * w.N * w.Hkv * w.D * 2 + w.B * w.N * 8 + w.B * w.N * w.Hq * w.D * 4
+
+
+def attention_flops(w, parents):
+    import numpy as np
+    depth_sum = 0
+    for par in parents:
+        d = np.zeros(len(par), dtype=np.int64)
+        for i in range(1, len(par)):
+            d[i] = d[par[i]] + 1
+        depth_sum += int((d + 1).sum())
+    return 4 * w.D * w.Hq * (w.B * w.N * w.L + depth_sum)
+
+
+def accept_bytes(w, greedy):
+    rows = w.N if greedy else 2 * w.N - 1
+    return w.B * rows * w.V * 4 + w.B * w.N * 4 * 2
+
+
+def time_calls(fns, steps, stream, torch):
+    """Events around each named call of every step; returns total ms and per-call mean ms."""
+    names = list(fns)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(steps):
+        e = evs[s]
+        e[0].record(stream)
+        for k, n in enumerate(names):
+            fns[n](s)
+            e[k + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end)
+    per = {n: sum(evs[s][k].elapsed_time(evs[s][k + 1]) for s in range(steps)) / steps for k, n in enumerate(names)}
+    return total, per
+
+
+def cpu_baseline(w, inputs, temperature, seconds):
+    """The oracle (numpy fp64 attention + C walk) on the host cores, on a bounded
+    sample: whole verification steps of this workload, repeated until about
+    ``seconds`` of CPU time has been spent (at least one step)."""
+    import numpy as np
+    import oracle
+    from workloads import bf16_to_f64
+    Q, Kc, Vc, Kt, Vt, q, p, draft, parent = inputs
+    host = [bf16_to_f64(t) for t in (Q, Kc, Vc, Kt, Vt)]
+    qn, pn, dn, parn = (t.cpu().numpy() for t in (q, p, draft, parent))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.tree_mask(parn)
+        oracle.tree_attention(*host, parn)
+        oracle.spec_accept(qn, pn, dn, parn, seed=0, temperature=temperature)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(steps * w.B * (w.N - 1) / el, 3), "unit": "tree-nodes/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{steps} full verification step(s) of the benchmark workload (mask + fp64 attention + "
+                      f"sampling walk at T={temperature}) in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (verification of independent "
+              f"sequences shards by batch with no communication).", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import token_tree_verification_amd as tv
+    from workloads import CONFIGS, CONFIG_TEXT, accept_inputs, attention_inputs
+
+    w = CONFIGS[args.config]
+    temps = [t for t in w.temperatures if t > 0]
+    T = args.temperature if args.temperature is not None else (temps[0] if temps else 1.0)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    parents = w.parents()
+    per_copy = attention_bytes(w) + accept_bytes(w, False)
+    ncopies = max(1, min(16, math.ceil(1.5 * MALL_BYTES / per_copy)))
+    copies, first_inputs = [], None
+    for c in range(ncopies):
+        Q, Kc, Vc, Kt, Vt = attention_inputs(w, device=dev, seed=w.data_seed + 100 * c)
+        q, p, draft, parent = accept_inputs(w, device=dev, seed=w.data_seed + 100 * c, parent=parents)
+        if c == 0:
+            first_inputs = (Q, Kc, Vc, Kt, Vt, q, p, draft, parent)
+        copies.append(dict(
+            sample=Step(tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, False, T, w.philox_seed, dev),
+            greedy=Step(tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, True, 1.0, w.philox_seed, dev)))
+    torch.cuda.synchronize()
+
+    def full(mode):
+        return lambda s: copies[s % ncopies][mode].run()
+
+    # warmup
+    for s in range(args.warmup):
+        copies[s % ncopies]["sample"].run()
+        copies[s % ncopies]["greedy"].run()
+    torch.cuda.synchronize()
+
+    # timed: whole steps, sampling mode (headline)
+    total_ms, _ = time_calls({"step": full("sample")}, args.steps, stream, torch)
+    ms_step = total_ms / args.steps
+    total_g, _ = time_calls({"step": full("greedy")}, args.steps, stream, torch)
+    ms_greedy = total_g / args.steps
+    # per-call durations inside the step (events on the launch stream)
+    _, per = time_calls({"mask": lambda s: copies[s % ncopies]["sample"].mask(),
+                         "attention": lambda s: copies[s % ncopies]["sample"].attention(),
+                         "accept": lambda s: copies[s % ncopies]["sample"].accept()}, args.steps, stream, torch)
+    _, per_g = time_calls({"accept_greedy": lambda s: copies[s % ncopies]["greedy"].accept()}, args.steps, stream,
+                          torch)
+
+    nodes = w.B * (w.N - 1)
+    value = nodes / (ms_step / 1e3)
+    a_bytes = attention_bytes(w)
+    a_flops = attention_flops(w, parents)
+    c_bytes = accept_bytes(w, False)
+    attn_gbs = a_bytes / (per["attention"] / 1e3) / 1e9
+    attn_tflops = a_flops / (per["attention"] / 1e3) / 1e12
+    acc_gbs = c_bytes / (per["accept"] / 1e3) / 1e9
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_bound = a_flops / a_bytes > ridge
+    dominant = "attention" if per["attention"] >= per["accept"] else "accept"
+    if dominant == "attention":
+        if mfma_bound:
+            roof = {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+        roof["kernel"] = "tv_tree_attention (tree_attention_kernel + attention_combine_kernel)"
+        roof["algorithmic_bytes"] = a_bytes
+        roof["avg_us"] = round(per["attention"] * 1e3, 3)
+    else:
+        roof = {"bound": "hbm", "achieved": round(acc_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(acc_gbs / HBM_PEAK_GBS, 4), "kernel": "tv_spec_accept (accept_stats + accept_walk)",
+                "algorithmic_bytes": c_bytes, "avg_us": round(per["accept"] * 1e3, 3)}
+    roof["traffic"] = None
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tree-nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {CONFIG_TEXT[w.name]}", "batch": w.B, "tree_nodes": w.N,
+                   "draft_nodes": w.N - 1, "heads_q_kv": [w.Hq, w.Hkv], "head_dim": w.D, "kv_len": w.L,
+                   "vocab": w.V, "mode": f"sampling T={T}", "input_copies": ncopies},
+        "roofline": roof,
+        "calls_us": {k: round(v * 1e3, 3) for k, v in {**per, **per_g}.items()},
+        "attention": {"GB/s": round(attn_gbs, 1), "TFLOP/s": round(attn_tflops, 3),
+                      "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "accept": {"GB/s": round(acc_gbs, 1), "hbm_frac": round(acc_gbs / HBM_PEAK_GBS, 4),
+                   "greedy_GB/s": round(accept_bytes(w, True) / (per_g["accept_greedy"] / 1e3) / 1e9, 1)},
+        "greedy": {"value": round(nodes / (ms_greedy / 1e3), 1), "ms_per_step": round(ms_greedy, 5)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, first_inputs, T, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -37,6 +37,11 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
+def _t32(T):
+    """The temperature as the C ABI receives it (binary32)."""
+    return float(np.float32(T))
+
+
 def _attn_check(got, ref, what):
     err = np.abs(got - ref).max()
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
@@ -202,7 +207,7 @@ def test_accept_tiny(tv, w):
         greedy = T == 0.0
         for seed in range(20):
             gpu = _accept_gpu(tv, q, None if greedy else p, draft, parent_t, seed, T if not greedy else 1.0, greedy)
-            ref = oracle.spec_accept(qn, None if greedy else pn, dn, parn, seed=seed, temperature=T or 1.0,
+            ref = oracle.spec_accept(qn, None if greedy else pn, dn, parn, seed=seed, temperature=_t32(T or 1.0),
                                      greedy=greedy)
             _compare_walk(gpu, ref, greedy)
             if greedy:
@@ -222,7 +227,7 @@ def test_accept_sampling_with_uniform_drafts(tv):
     for seed in range(30):
         for T in (1.0, 0.6):
             gpu = _accept_gpu(tv, tq, tp, td, tpar, seed, T, False)
-            ref = oracle.spec_accept(q, p, draft, par, seed=seed, temperature=T)
+            ref = oracle.spec_accept(q, p, draft, par, seed=seed, temperature=_t32(T))
             flips += _compare_walk(gpu, ref, False)
     assert flips <= FLIP_RATE * 60 * B * (N - 1)
 
@@ -239,7 +244,7 @@ def test_accept_edge_cases(tv):
         for greedy in (True, False):
             for seed in range(5):
                 gpu = _accept_gpu(tv, tq, tp, td, tpar, seed, 0.9, greedy)
-                ref = oracle.spec_accept(q, p, draft, par, seed=seed, temperature=0.9, greedy=greedy)
+                ref = oracle.spec_accept(q, p, draft, par, seed=seed, temperature=_t32(0.9), greedy=greedy)
                 _compare_walk(gpu, ref, greedy)
     bad = np.array([[-1, 0, 0], [-1, 2, 0]], np.int32)
     q = torch.zeros((2, 3, 10), device=dev())
@@ -264,7 +269,7 @@ def test_accept_full_config(tv, name):
         seeds = [0] if greedy else list(range(4 if w.B * w.V > 10 ** 7 else 16))
         for seed in seeds:
             gpu = _accept_gpu(tv, q, None if greedy else p, draft, parent_t, seed, T or 1.0, greedy)
-            ref = oracle.spec_accept(qn, None if greedy else pn, dn, parn, seed=seed, temperature=T or 1.0,
+            ref = oracle.spec_accept(qn, None if greedy else pn, dn, parn, seed=seed, temperature=_t32(T or 1.0),
                                      greedy=greedy)
             flips += _compare_walk(gpu, ref, greedy)
             nodes += w.B * (w.N - 1)
@@ -283,7 +288,7 @@ def test_accept_sampling_seed_sweep(tv, name):
     flips = 0
     for seed in range(nseeds):
         gpu = _accept_gpu(tv, q, p, draft, parent_t, seed, T, False)
-        ref = oracle.spec_accept(qn, pn, dn, parn, seed=seed, temperature=T)
+        ref = oracle.spec_accept(qn, pn, dn, parn, seed=seed, temperature=_t32(T))
         flips += _compare_walk(gpu, ref, False)
     nodes = nseeds * w.B * (w.N - 1)
     assert flips <= FLIP_RATE * nodes
