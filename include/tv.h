@@ -147,7 +147,14 @@ int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t
  *   out_tokens     int32 [B,N] out: accepted tokens then the extra token, -1 padded.
  * Sizes: B >= 0, 1 <= N <= TV_MAX_NODES, V >= 1.  Logits must be finite.
  * Workspace: at least tv_spec_accept_workspace(B,N,V,greedy) bytes, 256-byte
- * aligned.
+ * aligned, zero-filled before its first use.  The call keeps its team barrier
+ * words there (generation-tagged, so they never need clearing again): the
+ * same workspace can be reused by later calls of any shape without clearing.
+ * The size depends on the current device (it is planned for the device's
+ * resident workgroup capacity).
+ * Execution: one launch sized to the device's resident workgroup capacity;
+ * every sequence is walked by a team of workgroups that synchronise through
+ * the workspace, so calls that share a workspace must not overlap.
  */
 size_t tv_spec_accept_workspace(int B, int N, int V, int greedy);
 int tv_spec_accept(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,

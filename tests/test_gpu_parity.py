@@ -232,6 +232,29 @@ def test_accept_sampling_with_uniform_drafts(tv):
     assert flips <= FLIP_RATE * 60 * B * (N - 1)
 
 
+def test_accept_workspace_sizes(tv):
+    g = tv.accept_workspace_bytes(1, 6, 128256, True)
+    s = tv.accept_workspace_bytes(1, 6, 128256, False)
+    assert 0 < g < s and s >= 2 * 128256 * 8
+
+
+def test_accept_reuses_workspace_across_calls(tv):
+    """The team barrier words live in the workspace and are never cleared:
+    repeated calls on one workspace must all match the oracle."""
+    w = CONFIGS["c2"]
+    q, p, draft, parent_t = accept_inputs(w, device=dev())
+    qn, pn, dn, parn = _np(q), _np(p), _np(draft), _np(parent_t)
+    ws = torch.zeros(max(tv.accept_workspace_bytes(1, 6, 128256, False), 1 << 20), dtype=torch.uint8, device=dev())
+    for seed in range(12):
+        a, n, t = tv.spec_accept(q, p, draft, parent_t, seed=seed, temperature=1.0, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.spec_accept(qn, pn, dn, parn, seed=seed, temperature=1.0)
+        _compare_walk((_np(a), _np(n), _np(t)), ref, False)
+    # team 0's control line: [0] generation (one per call), [2] barrier time-out flag
+    ctrl = _np(ws[:128].view(torch.int64))
+    assert ctrl[0] == 12 and ctrl[2] == 0
+
+
 def test_accept_edge_cases(tv):
     rng = np.random.default_rng(8)
     # root only: extra token from the root row; V = 1; invalid tree

@@ -92,13 +92,15 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    """Caller-supplied workspace, or a fresh zero-filled one (the accept call
+    keeps its control words in the workspace and needs them zero at first use)."""
     if nbytes == 0:
         return None
     if workspace is not None:
         if workspace.device != device or workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace must hold {nbytes} bytes on {device}")
         return workspace
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def build_tree_mask(parent: torch.Tensor):

@@ -43,6 +43,31 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t node, ui
     return (float)(r.x >> 8) * (1.0f / 16777216.0f);
 }
 
+// exp(y) for y <= 0 to ~1e-15 relative, in fp64: y = (k/32) ln 2 + r with
+// k = rint(32 y / ln 2) (Cody-Waite reduction, ln 2 / 32 split into a double
+// and its remainder), exp(r) by its degree-5 Taylor polynomial (|r| <= ln2/64,
+// truncation < 3e-15), and 2^(k/32) = 2^(k >> 5) * tab[k & 31] where
+// tab[j] = 2^(j/32) comes from exp2_table().  Returns 0 below -745.
+__host__ __device__ __forceinline__ double exp_nonpos(double y, const double* tab) {
+    if (!(y > -745.0)) return 0.0;
+    const double kInv = 0x1.71547652b82fep+5;   // 32 / ln 2
+    const double kLhi = 0x1.62e42fefa39efp-6;   // ln 2 / 32, rounded to double
+    const double kLlo = 0x1.abc9e3b39803fp-61;  // ln 2 / 32 - kLhi
+    const double kd = rint(y * kInv);
+    const int k = (int)kd;
+    double r = fma(-kd, kLhi, y);
+    r = fma(-kd, kLlo, r);
+    double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+    p = fma(r, p, 1.0 / 6.0);
+    p = fma(r, p, 0.5);
+    p = fma(r, p, 1.0);
+    p = fma(r, p, 1.0);
+    return ldexp(tab[k & 31] * p, k >> 5);
+}
+
+// tab[j] = 2^(j/32), j = 0..31 (from the library's exp2).
+__host__ __device__ __forceinline__ void exp2_table(double* tab, int j) { tab[j] = exp2((double)j / 32.0); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
