@@ -97,13 +97,16 @@ int tv_build_tree_mask(const int32_t* parent, int B, int N, uint64_t* anc_mask, 
  *   V_tree   bf16 [B,N,Hkv,D]     values of the tree nodes.
  *   anc_mask uint64 [B,N]         from tv_build_tree_mask; must describe a valid tree.
  *   out      fp32 [B,N,Hq,D]      out.
- *   scale    softmax scale, conventionally 1/sqrt(D); must be finite.
+ *   scale    softmax scale, conventionally 1/sqrt(D); finite and > 0.
  * Sizes: B >= 0, 1 <= N <= TV_MAX_NODES, Hq >= Hkv >= 1 with Hq % Hkv == 0,
  * D == TV_HEAD_DIM, L >= 0.
  * Numerics: QK^T in bf16 with fp32 accumulation, softmax in fp32, P.V with
  * P and V in fp16 and fp32 accumulation.  Precondition: |V| <= 65504.
  * Workspace: at least tv_tree_attention_workspace(...) bytes, 256-byte aligned
- * (may be NULL when that size is 0).
+ * (may be NULL when that size is 0), zero-filled before its first use: when the
+ * cache is split across workgroups it holds their partial results and one
+ * arrival counter per row tile, which the last workgroup resets to zero.
+ * Calls that share a workspace must not overlap.
  */
 size_t tv_tree_attention_workspace(int B, int N, int Hq, int Hkv, int D, int L);
 int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t* V_cache,
