@@ -17,8 +17,10 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
+import hashlib
 import math
 import os
+import re
 import sys
 import time
 
@@ -30,6 +32,9 @@ METRIC = "verified tree-nodes/sec + achieved HBM GB/s & MFMA util vs MI355X peak
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
+COPY_CAL_BYTES = 512 << 20
+ATTN_SOURCES = ("token_tree_verification_amd/csrc/tv_attention.hip", "token_tree_verification_amd/csrc/tv_device.h")
+ACC_SOURCES = ("token_tree_verification_amd/csrc/tv_accept.hip", "token_tree_verification_amd/csrc/tv_device.h")
 
 
 def parse():
@@ -41,13 +46,14 @@ def parse():
     ap.add_argument("--temperature", type=float, default=None, help="sampling temperature (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP-graph replays")
     return ap.parse_args()
 
 
 class Step:
     """Pre-marshalled C-ABI calls of one verification step on one input copy."""
 
-    def __init__(self, tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, greedy, temperature, seed, dev):
+    def __init__(self, tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, greedy, temperature, seed, dev, stream):
         import torch
         self.lib = tv.library()
         B, N, Hq, Hkv, D, L, V = w.B, w.N, w.Hq, w.Hkv, w.D, w.L, w.V
@@ -64,7 +70,7 @@ class Step:
         cw = tv.accept_workspace_bytes(B, N, V, greedy)
         self.acc_ws = torch.zeros(max(cw, 256), dtype=torch.uint8, device=dev)
         P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
-        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        self.stream = ctypes.c_void_p(stream.cuda_stream)
         self.mask_args = (P(parent), B, N, P(self.anc), P(self.depth), P(self.status), self.stream)
         self.attn_args = (P(Q), P(Kc), P(Vc), P(Kt), P(Vt), P(self.anc), P(self.out), B, N, Hq, Hkv, D, L,
                           ctypes.c_float(1.0 / math.sqrt(D)), P(self.attn_ws), ctypes.c_size_t(aw), self.stream)
@@ -92,6 +98,13 @@ class Step:
         self.attention()
         self.accept()
 
+    def capture(self, torch, stream):
+        """Record the three calls of the step into a HIP graph on `stream`."""
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=stream):
+            self.run()
+        return self.graph
+
 
 def attention_bytes(w):
     kv = 2 * w.B * w.Hkv * w.L * w.D * 2
@@ -114,13 +127,32 @@ def accept_bytes(w, greedy):
     return w.B * rows * w.V * 4 + w.B * w.N * 4 * 2
 
 
-def time_calls(fns, steps, stream, torch):
-    """Events around each named call of every step; returns total ms and per-call mean ms."""
+def sleep_cycles_per_ms(torch, stream):
+    """Shader-clock cycles of torch's spin kernel per millisecond on this device."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    cyc = 2_000_000
+    torch.cuda._sleep(cyc)  # first launch pays the module load
+    torch.cuda.synchronize()
+    a.record(stream)
+    torch.cuda._sleep(cyc)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return cyc / max(a.elapsed_time(b), 1e-3)
+
+
+def time_calls(fns, steps, stream, torch, lead_cycles):
+    """Events around each named call of every step; returns total ms and per-call mean ms.
+
+    A spin kernel of ``lead_cycles`` runs first, so the host has queued every
+    call before the device reaches them: the event pairs then bracket device
+    time only, not host launch latency."""
     names = list(fns)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(lead_cycles))
     start.record(stream)
     for s in range(steps):
         e = evs[s]
@@ -133,6 +165,42 @@ def time_calls(fns, steps, stream, torch):
     total = start.elapsed_time(end)
     per = {n: sum(evs[s][k].elapsed_time(evs[s][k + 1]) for s in range(steps)) / steps for k, n in enumerate(names)}
     return total, per
+
+
+def copy_calibration(torch, dev, nbytes=COPY_CAL_BYTES):
+    """One plain elementwise copy (read nbytes, write nbytes) outside the timed
+    region: under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the factor
+    that turns those counters into bytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def kernel_sources_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload, kernel_key, files):
+    """HBM bytes per launch of ``kernel_key`` on ``workload`` from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get("kernels", {}).get(kernel_key)
+    if not rec or rec.get("sources_sha256") != kernel_sources_digest(files):
+        return None
+    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
 
 def cpu_baseline(w, inputs, temperature, seconds):
@@ -182,7 +250,8 @@ def main():
     T = args.temperature if args.temperature is not None else (temps[0] if temps else 1.0)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.Stream(dev)  # every call of the step is issued (and captured) here
+    torch.cuda.set_stream(stream)
 
     parents = w.parents()
     per_copy = attention_bytes(w) + accept_bytes(w, False)
@@ -194,30 +263,48 @@ def main():
         if c == 0:
             first_inputs = (Q, Kc, Vc, Kt, Vt, q, p, draft, parent)
         copies.append(dict(
-            sample=Step(tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, False, T, w.philox_seed, dev),
-            greedy=Step(tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, True, 1.0, w.philox_seed, dev)))
+            sample=Step(tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, False, T, w.philox_seed, dev, stream),
+            greedy=Step(tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, True, 1.0, w.philox_seed, dev, stream)))
     torch.cuda.synchronize()
 
-    def full(mode):
-        return lambda s: copies[s % ncopies][mode].run()
-
-    # warmup
+    # warmup (eager), then record one graph per input copy and mode
     for s in range(args.warmup):
         copies[s % ncopies]["sample"].run()
         copies[s % ncopies]["greedy"].run()
     torch.cuda.synchronize()
+    use_graph = not args.eager
+    if use_graph:
+        for c in copies:
+            c["sample"].capture(torch, stream)
+            c["greedy"].capture(torch, stream)
+        torch.cuda.synchronize()
+        for s in range(args.warmup):
+            copies[s % ncopies]["sample"].graph.replay()
+            copies[s % ncopies]["greedy"].graph.replay()
+        torch.cuda.synchronize()
+
+    def full(mode):
+        if use_graph:
+            return lambda s: copies[s % ncopies][mode].graph.replay()
+        return lambda s: copies[s % ncopies][mode].run()
+
+    copy_calibration(torch, dev)
+    cyc_ms = sleep_cycles_per_ms(torch, stream)
+    # enough lead for the host to queue every call of the timed loop
+    lead = lambda calls: cyc_ms * max(2.0, 0.05 * calls)
 
     # timed: whole steps, sampling mode (headline)
-    total_ms, _ = time_calls({"step": full("sample")}, args.steps, stream, torch)
+    total_ms, _ = time_calls({"step": full("sample")}, args.steps, stream, torch, lead(args.steps))
     ms_step = total_ms / args.steps
-    total_g, _ = time_calls({"step": full("greedy")}, args.steps, stream, torch)
+    total_g, _ = time_calls({"step": full("greedy")}, args.steps, stream, torch, lead(args.steps))
     ms_greedy = total_g / args.steps
-    # per-call durations inside the step (events on the launch stream)
+    # per-call durations inside the step (events on the launch stream, device time only)
     _, per = time_calls({"mask": lambda s: copies[s % ncopies]["sample"].mask(),
                          "attention": lambda s: copies[s % ncopies]["sample"].attention(),
-                         "accept": lambda s: copies[s % ncopies]["sample"].accept()}, args.steps, stream, torch)
+                         "accept": lambda s: copies[s % ncopies]["sample"].accept()}, args.steps, stream, torch,
+                        lead(3 * args.steps))
     _, per_g = time_calls({"accept_greedy": lambda s: copies[s % ncopies]["greedy"].accept()}, args.steps, stream,
-                          torch)
+                          torch, lead(args.steps))
 
     nodes = w.B * (w.N - 1)
     value = nodes / (ms_step / 1e3)
@@ -237,14 +324,17 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
-        roof["kernel"] = "tv_tree_attention (tree_attention_kernel + attention_combine_kernel)"
+        roof["kernel"] = "tv::tree_attention_kernel (tv_tree_attention, one launch)"
         roof["algorithmic_bytes"] = a_bytes
+        roof["algorithmic_flops"] = a_flops
         roof["avg_us"] = round(per["attention"] * 1e3, 3)
+        roof["traffic"] = counted_traffic(w.name, "tree_attention_kernel", ATTN_SOURCES)
     else:
         roof = {"bound": "hbm", "achieved": round(acc_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(acc_gbs / HBM_PEAK_GBS, 4), "kernel": "tv_spec_accept (accept_stats + accept_walk)",
+                "frac": round(acc_gbs / HBM_PEAK_GBS, 4),
+                "kernel": "tv::spec_accept_kernel<false, true> (tv_spec_accept sampling, one launch)",
                 "algorithmic_bytes": c_bytes, "avg_us": round(per["accept"] * 1e3, 3)}
-    roof["traffic"] = None
+        roof["traffic"] = counted_traffic(w.name, "spec_accept_kernel<false, true>", ACC_SOURCES)
 
     res = {
         "metric": METRIC,
@@ -261,7 +351,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {CONFIG_TEXT[w.name]}", "batch": w.B, "tree_nodes": w.N,
                    "draft_nodes": w.N - 1, "heads_q_kv": [w.Hq, w.Hkv], "head_dim": w.D, "kv_len": w.L,
-                   "vocab": w.V, "mode": f"sampling T={T}", "input_copies": ncopies},
+                   "vocab": w.V, "mode": f"sampling T={T}", "input_copies": ncopies,
+                   "launch": "hip-graph replay" if use_graph else "eager"},
         "roofline": roof,
         "calls_us": {k: round(v * 1e3, 3) for k, v in {**per, **per_g}.items()},
         "attention": {"GB/s": round(attn_gbs, 1), "TFLOP/s": round(attn_tflops, 3),

@@ -315,3 +315,45 @@ def test_accept_sampling_seed_sweep(tv, name):
         flips += _compare_walk(gpu, ref, False)
     nodes = nseeds * w.B * (w.N - 1)
     assert flips <= FLIP_RATE * nodes
+
+
+def test_graph_replay_matches_eager(tv):
+    """The three calls captured in one HIP graph and replayed repeatedly, with
+    eager work in between, give the eager results every time (the accept and
+    attention workspaces keep self-resetting control words)."""
+    w = CONFIGS["c2"]
+    par = w.parents().astype(np.int32)
+    s = torch.cuda.Stream(dev())
+    with torch.cuda.stream(s):
+        Q, Kc, Vc, Kt, Vt = attention_inputs(w, device=dev())
+        q, p, draft, parent_t = accept_inputs(w, device=dev(), parent=par)
+        anc_ws = torch.zeros(max(tv.attention_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.L), 256),
+                             dtype=torch.uint8, device=dev())
+        acc_ws = torch.zeros(tv.accept_workspace_bytes(w.B, w.N, w.V, False), dtype=torch.uint8, device=dev())
+        out = torch.empty((w.B, w.N, w.Hq, w.D), dtype=torch.float32, device=dev())
+        outs = (torch.empty((w.B,), dtype=torch.int32, device=dev()),
+                torch.empty((w.B, w.N), dtype=torch.int32, device=dev()),
+                torch.empty((w.B, w.N), dtype=torch.int32, device=dev()))
+
+        def step(seed):
+            anc, _, _ = tv.build_tree_mask(parent_t)
+            tv.tree_attention(Q, Kc, Vc, Kt, Vt, anc, out=out, workspace=anc_ws)
+            tv.spec_accept(q, p, draft, parent_t, seed=seed, temperature=1.0, workspace=acc_ws, outputs=outs)
+
+        step(3)
+        torch.cuda.synchronize()
+        ref = [out.clone()] + [o.clone() for o in outs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step(3)
+        for rep in range(5):
+            out.zero_()
+            for o in outs:
+                o.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref[0]), f"attention differs on replay {rep}"
+            for o, r in zip(outs, ref[1:]):
+                assert torch.equal(o, r), f"accept differs on replay {rep}"
+            step(rep + 10)  # eager calls on the same workspaces between replays
+            torch.cuda.synchronize()
