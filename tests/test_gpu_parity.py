@@ -235,7 +235,11 @@ def test_accept_sampling_with_uniform_drafts(tv):
 def test_accept_workspace_sizes(tv):
     g = tv.accept_workspace_bytes(1, 6, 128256, True)
     s = tv.accept_workspace_bytes(1, 6, 128256, False)
-    assert 0 < g < s and s >= 2 * 128256 * 8
+    assert 0 < g < s
+    # sampling keeps each member's residual slice on chip: no vocabulary-sized rows in the workspace
+    assert s < 4 << 20
+    # vocabularies whose slices cannot fit a team's on-chip residual are refused
+    assert tv.accept_workspace_bytes(1, 6, 256 * 8192 + 1, False) == 0
 
 
 def test_accept_reuses_workspace_across_calls(tv):

@@ -11,24 +11,29 @@
 // One launch.  A team of W workgroups owns one sequence at a time; member w
 // owns vocabulary slice w of every logit row.
 //  1. Statistics: each member streams its slice of every row once (coalesced
-//     16-byte loads, several rows in flight per wave) and publishes the slice
-//     max and sum of exp((x - max)/T) -- or the max and its first index in
-//     greedy mode.  Rows whose exact normaliser is likely needed (all rows of
-//     small problems, otherwise the root's target row and the draft rows of
-//     its children) also get an fp64 slice sum.
-//  2. Team barrier.  Every member then runs the same walk redundantly: the
-//     decisions only need merged row statistics and a few gathered logits,
-//     so all members agree bit for bit without communicating.
-//  3. A rejection needs vocabulary passes: missing fp64 normalisers of the
-//     parent target and the rejected child's draft row, then the residual
-//     max(0, R - P_c) over the slices in fp64 (kept per team), each followed by
-//     a team barrier.  The residual pass also forms the next sibling's fp64
-//     normaliser in case it is rejected too.
-//  4. The extra token: every member publishes the fp64 mass of its slice, and
-//     the member whose slice holds U * total scans it to find the token.
-// fp64 in steps 3-4 keeps inverse-CDF boundaries within ~1e-15 of the exact
-// values: with 1e5-token vocabularies fp32 masses move a boundary by ~1e-7,
-// which changes the drawn token far more often.
+//     16-byte loads, prefetched a group ahead, every row's slice spread over
+//     the four waves) and publishes the slice max and sum of
+//     exp((x - max)/T) -- or the max and its first index in greedy mode.
+//     The logits the walk tests, q_parent(c)(x_c) and p_c(x_c), are gathered
+//     while the stream is in flight.
+//  2. Greedy: the last member to publish (arrival counter per sequence) merges
+//     the argmax of every target row and writes the path; nobody waits.
+//  3. Sampling: one team barrier, then every member merges the statistics of
+//     every row and runs the same walk redundantly: decisions need only the
+//     merged statistics and the gathered logits, so all members agree bit for
+//     bit without communicating.
+//  4. A rejection costs one pass over the slices: the residual
+//     max(0, R - P_c) replaces the member's slice of R in LDS, its slice mass
+//     and the residual at the next sibling's token are published, and a team
+//     barrier follows.
+//  5. The extra token: every member knows every slice's mass (from the last
+//     residual pass, or from the statistics when drawing from a target row),
+//     so the member whose slice holds U * total scans its slice alone.
+// Precision: per-element exponentials are fp32 (v_exp_f32 of (x - max) * c,
+// with the subtraction first so the heavy terms carry ~1e-7 relative error);
+// sums and masses accumulate in fp64; the accept ratio is formed in fp64 from
+// the gathered logits.  Decisions can differ from exact arithmetic only within
+// ~1e-6 of a boundary.
 //
 // Team barrier: members store a generation-tagged arrival word, member 0
 // gathers them and stores one release word.  Data crossing members goes
@@ -53,18 +58,18 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxTeamSize = 256;
 constexpr int kMaxTeams = 1024;
-constexpr int kMinSlice = 512;       // logits per member and row, at least
-constexpr int kCtrlLine = 16;        // u64 words per team: [0] generation, [1] release, [2] error
-constexpr int kP64Slots = 4;         // fp64 values a member publishes per phase
+constexpr int kMinSlice = 1024;      // logits per member and row, at least
+constexpr int kMaxSlice = 8192;      // sampling: a member's residual slice lives in LDS (32 KB)
+constexpr int kSpan = 4 * kWave;     // logits one wave covers with one 16-byte load per lane
+constexpr int kGroup = 4;            // spans per prefetch group (two groups in flight per wave)
+constexpr int kCtrlLine = 16;        // u64 words per team: [0] generation, [1] release, [2] time-out flag
 constexpr int kTagShift = 24;        // barrier tag = (generation << 24) + barrier index
 constexpr uint32_t kSpinLimit = 1u << 20;
-constexpr long kSmallWork = 1L << 24;  // logits below which every row gets an fp64 sum in step 1
-constexpr int kRowsInFlight = 2;     // rows a wave streams together in step 1
-constexpr int kVecPerRow = 4;        // float4 loads per lane and row per step-1 chunk
+constexpr int kMassRec = 4;          // doubles per (pass, member): mass, new and old residual at the next token
 
 struct AcceptPlan {
     int W, nteams, slice;
-    size_t ctrl_off, arrive_off, stats_off, stats64_off, p64_off, rbuf_off, total;
+    size_t ctrl_off, arrive_off, counter_off, stats_off, mass_off, total;
 };
 
 struct AccArgs {
@@ -75,15 +80,14 @@ struct AccArgs {
     int32_t* accept_len;
     int32_t* accepted;
     int32_t* tokens;
-    uint64_t* ctrl;     // [kMaxTeams][kCtrlLine]
-    uint64_t* arrive;   // [kMaxTeams][kMaxTeamSize]
-    uint64_t* stats;    // [nteams][2][2N][W] packed (max, sum) or (max, argmax)
-    double* stats64;    // [nteams][2][2N][W] fp64 slice sums of exp((x - slice max)/T)
-    double* p64;        // [nteams][2][kP64Slots][W]
-    double* rbuf;       // [nteams][2][V]
-    int B, N, V, W, slice, nteams, all64;
-    float inv_t;
-    double inv_t64;
+    uint64_t* ctrl;      // sampling: [kMaxTeams][kCtrlLine]
+    uint64_t* arrive;    // sampling: [kMaxTeams][kMaxTeamSize]
+    uint32_t* counter;   // greedy: [B] arrivals per sequence, reset by the last arriver
+    uint64_t* stats;     // sampling: [nteams][2][2N][W] (max, sum); greedy: [B][N][W] (max, index)
+    double* mass;        // sampling: [nteams][N][W][kMassRec]
+    int B, N, V, W, slice, nteams;
+    float c;             // log2(e) / T
+    double inv_t64;      // 1 / T
     uint64_t seed;
 };
 
@@ -113,7 +117,7 @@ struct TeamSync {
     uint32_t k;        // barriers passed so far in this call
 };
 
-__device__ void team_sync(TeamSync& s, int w, int W) {
+__device__ __forceinline__ void team_sync(TeamSync& s, int w, int W) {
     ++s.k;
     const uint64_t tag = s.base + s.k;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's device-scope stores have landed
@@ -150,17 +154,10 @@ __device__ void team_sync(TeamSync& s, int w, int W) {
 }
 
 // ------------------------------------------------------------------ helpers --
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 // Block scan in fp64 with a fixed association (identical on every member):
 // shuffle scan per wave, then the wave totals in order.  Returns the inclusive
-// value; `excl` receives the exclusive one, bitwise equal to the previous
-// thread's inclusive value, and `tot` the block total.  `wt` is LDS for the
-// kWaves wave totals.
+// value; `excl` receives the exclusive one and `tot` the block total.  `wt` is
+// LDS for the kWaves wave totals.
 __device__ __forceinline__ double block_scan_d(double v, double* wt, double& excl, double& tot) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -197,219 +194,387 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
     }
 }
 
-// Sum of the W values published in one slot, identical on every member.
-__device__ double gather_sum(const double* slot, int W, double* wt) {
-    const double v = (int)threadIdx.x < W ? ld_dev_d(&slot[threadIdx.x]) : 0.0;
-    return block_sum_d(v, wt);
-}
-
 // exp((x - m) / T) in fp64 for x <= m.
 __device__ __forceinline__ double exp_scaled(float x, float m, double inv_t64, const double* tab) {
     return exp_nonpos(((double)x - (double)m) * inv_t64, tab);
 }
 
-// ------------------------------------------------------------ step 1 pieces --
-struct RowAcc {
-    float m, s, bv;
-    int bi;
-    double s64;
-};
+// Storage index of the i-th streamed row: target rows 0..N-1, then draft rows
+// 1..N-1 stored at N + c.
+__device__ __forceinline__ int stat_row(int i, int N) { return i < N ? i : i + 1; }
 
-// Streams up to kRowsInFlight rows of this member's slice with one wave and
-// leaves the wave-merged result in every lane (sampling: max, sum, optional
-// fp64 sum; greedy: max and first argmax).
+// Row pointer of a storage index: q row u at u, p row c at N + c.
+__device__ __forceinline__ const float* row_ptr(const float* qb, const float* pb, int r, int N, int V) {
+    return r < N ? qb + (size_t)r * V : pb + (size_t)(r - N) * V;
+}
+
+// ------------------------------------------------------- 1. statistics pass --
+// Wave k streams rows k, k + 4, ... (storage order: target rows, then draft
+// rows) over this member's slice, one 16-byte load per lane per span, a
+// prefetch group ahead of the arithmetic, and publishes each row's slice
+// statistics as soon as the row ends: sampling (max, sum of exp((x - max) c),
+// accumulated in fp64, stored as fp32), greedy (max, first index).
 template <bool GREEDY, bool VEC4>
-__device__ void stream_rows(const float* const* rows, const bool* want64, int nr, int s0, int s1, int lane,
-                            float inv_t, double inv_t64, const double* tab, RowAcc* acc) {
+__device__ __forceinline__ void stream_slices(const float* qb, const float* pb, int nrows, int N, int V, int s0,
+                                              int nsl, float c, uint64_t* stats, int W, int w) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nspan = (nsl + kSpan - 1) / kSpan;
+    const int myrows = wave < nrows ? (nrows - wave + kWaves - 1) / kWaves : 0;
+    if (myrows == 0) return;
+
+    // Load cursor (row lr of this wave, span lj) and process cursor (pr, pj).
+    // Loads are unconditional so that several stay in flight: past the last
+    // item the cursor stays on it, and lanes past the slice end read its last
+    // vector and then see -inf.
+    int lr = 0, lj = 0, pr = 0, pj = 0;
+    const int last_lr = myrows - 1, last_lj = nspan - 1;
+    auto load = [&](f32x4& x) {
+        const float* row = row_ptr(qb, pb, stat_row(wave + kWaves * lr, N), N, V) + s0;
+        const int e = lj * kSpan;  // first element of the span within the slice
+        if constexpr (VEC4) {
+            const int v = e + 4 * lane;
+            const f32x4 t = *reinterpret_cast<const f32x4*>(row + min(v, nsl - 4));
 #pragma unroll
-    for (int r = 0; r < kRowsInFlight; ++r) {
-        acc[r].m = -INFINITY;
-        acc[r].s = 0.f;
-        acc[r].bv = -INFINITY;
-        acc[r].bi = 0x7fffffff;
-        acc[r].s64 = 0.0;
-    }
-    constexpr int kStep = VEC4 ? 4 * kWave * kVecPerRow : kWave * kVecPerRow;
-    for (int c0 = s0; c0 < s1; c0 += kStep) {
-        float x[kRowsInFlight][4 * kVecPerRow];
-        // issue every load of the chunk first
+            for (int k = 0; k < 4; ++k) x[k] = v < nsl ? t[k] : -INFINITY;
+        } else {
 #pragma unroll
-        for (int r = 0; r < kRowsInFlight; ++r) {
-#pragma unroll
-            for (int j = 0; j < kVecPerRow; ++j) {
-                if constexpr (VEC4) {
-                    const int v = c0 + 4 * (lane + kWave * j);
-                    f32x4 t = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                    if (r < nr && v < s1) t = *reinterpret_cast<const f32x4*>(rows[r] + v);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[r][4 * j + e] = t[e];
-                } else {
-                    const int v = c0 + lane + kWave * j;
-                    x[r][4 * j] = (r < nr && v < s1) ? rows[r][v] : -INFINITY;
-#pragma unroll
-                    for (int e = 1; e < 4; ++e) x[r][4 * j + e] = -INFINITY;
-                }
+            for (int k = 0; k < 4; ++k) {
+                const int v = e + lane + kWave * k;
+                const float t = row[min(v, nsl - 1)];
+                x[k] = v < nsl ? t : -INFINITY;
             }
         }
-#pragma unroll
-        for (int r = 0; r < kRowsInFlight; ++r) {
-            if (r >= nr) continue;
-            RowAcc& A = acc[r];
-            if constexpr (GREEDY) {
-#pragma unroll
-                for (int j = 0; j < kVecPerRow; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int v = VEC4 ? c0 + 4 * (lane + kWave * j) + e : c0 + lane + kWave * j;
-                        if (x[r][4 * j + e] > A.bv) {  // indices increase along a lane: first maximum kept
-                            A.bv = x[r][4 * j + e];
-                            A.bi = v;
-                        }
-                    }
-            } else {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 4 * kVecPerRow; ++i) mx = fmaxf(mx, x[r][i]);
-                if (mx > A.m) {
-                    if (A.m != -INFINITY) {
-                        A.s *= __expf((A.m - mx) * inv_t);
-                        if (want64[r]) A.s64 *= exp_scaled(A.m, mx, inv_t64, tab);
-                    }
-                    A.m = mx;
-                }
-                if (A.m != -INFINITY) {
-#pragma unroll
-                    for (int i = 0; i < 4 * kVecPerRow; ++i) A.s += __expf((x[r][i] - A.m) * inv_t);
-                    if (want64[r]) {
-#pragma unroll
-                        for (int i = 0; i < 4 * kVecPerRow; ++i) A.s64 += exp_scaled(x[r][i], A.m, inv_t64, tab);
-                    }
-                }
-            }
+        const bool at_end = lr == last_lr && lj == last_lj;
+        lj = at_end ? lj : (lj == last_lj ? 0 : lj + 1);
+        lr = at_end ? lr : (lj == 0 ? lr + 1 : lr);
+    };
+
+    float m = -INFINITY, bv = -INFINITY;
+    double s = 0.0;
+    int bi = 0x7fffffff;
+    auto process = [&](const f32x4& x) {
+        if (pj == 0) {
+            m = -INFINITY;
+            s = 0.0;
+            bv = -INFINITY;
+            bi = 0x7fffffff;
         }
-    }
-    // wave merge
-#pragma unroll
-    for (int r = 0; r < kRowsInFlight; ++r) {
-        if (r >= nr) continue;
-        RowAcc& A = acc[r];
+        const int e = pj * kSpan;
         if constexpr (GREEDY) {
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) argmax_merge(A.bv, A.bi, __shfl_xor(A.bv, o), __shfl_xor(A.bi, o));
+            for (int k = 0; k < 4; ++k) {
+                const int v = VEC4 ? e + 4 * lane + k : e + lane + kWave * k;  // increasing along the lane
+                if (x[k] > bv) {
+                    bv = x[k];
+                    bi = s0 + v;
+                }
+            }
         } else {
-            const float M = wave_max(A.m);
-            const double f64 = (A.m == -INFINITY) ? 0.0 : exp_scaled(A.m, M, inv_t64, tab);
-            const float f32 = (A.m == -INFINITY) ? 0.f : __expf((A.m - M) * inv_t);
-            A.s = wave_sum(A.s * f32);
-            if (want64[r]) A.s64 = wave_sum_d(A.s64 * f64);
-            A.m = M;
+            const float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            if (cm > m) {
+                if (m != -INFINITY) s *= (double)__builtin_amdgcn_exp2f((m - cm) * c);
+                m = cm;
+            }
+            if (m != -INFINITY) {
+                const float e0 = __builtin_amdgcn_exp2f((x[0] - m) * c) + __builtin_amdgcn_exp2f((x[1] - m) * c);
+                const float e1 = __builtin_amdgcn_exp2f((x[2] - m) * c) + __builtin_amdgcn_exp2f((x[3] - m) * c);
+                s += (double)(e0 + e1);
+            }
+        }
+        if (pj == nspan - 1) {  // the row is done: reduce over the wave and publish
+            const int r = stat_row(wave + kWaves * pr, N);
+            if constexpr (GREEDY) {
+                group_argmax_dpp(bv, bi, kWave);
+                if (lane == 0) st_dev(&stats[(size_t)r * W + w], pack2(bv, __int_as_float(bi)));
+            } else {
+                const float M = group_max_dpp(m, kWave);
+                const double f = (m == -INFINITY) ? 0.0 : (double)__builtin_amdgcn_exp2f((m - M) * c);
+                const double S = group_sum_dpp(s * f, kWave);
+                if (lane == 0) st_dev(&stats[(size_t)r * W + w], pack2(M, (float)S));
+            }
+        }
+        if (++pj == nspan) {
+            pj = 0;
+            ++pr;
+        }
+    };
+
+    f32x4 xa[kGroup], xb[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) load(xa[i]);
+    while (pr < myrows) {
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) load(xb[i]);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i)
+            if (pr < myrows) process(xa[i]);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) load(xa[i]);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i)
+            if (pr < myrows) process(xb[i]);
+    }
+}
+
+// ------------------------------------------------------- merge of statistics --
+// Lanes are grouped LPR to a row (LPR = W rounded up to a power of two, at most
+// 64); each lane takes members lane % LPR + LPR * i.  Group-local shuffles
+// reduce; rows are taken 64 / LPR per wave and several batches are in flight.
+__device__ __forceinline__ int lanes_per_row(int W) {
+    int l = 1;
+    while (l < W && l < kWave) l <<= 1;
+    return l;
+}
+
+
+// Sampling: merged max sM[r] and normaliser sS[r] = sum_w s_w exp((m_w - M)/T)
+// of every streamed row, from stats[r][W].  Each wave issues the loads of
+// kBatch row groups before reducing any of them.  The factors are fp32
+// (relative error ~1e-7), the sums fp64.
+constexpr int kBatch = 4;
+
+__device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows, int N, int W, float c, float* sM,
+                                               double* sS) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lpr = lanes_per_row(W);
+    const int rpw = kWave / lpr;              // rows per wave per group
+    const int per = (W + lpr - 1) / lpr;      // members per lane (<= 4)
+    const int g = lane / lpr, li = lane % lpr;
+    for (int r0 = wave * rpw * kBatch; r0 < nrows; r0 += kWaves * rpw * kBatch) {
+        // loads are unconditional (indices clamped) so that they all stay in flight
+        uint64_t e[kBatch][4];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int ri = r0 + k * rpw + g;
+            const int r = stat_row(min(ri, nrows - 1), N);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[k][i] = ld_dev(&stats[(size_t)r * W + min(li + lpr * i, W - 1)]);
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int ri = r0 + k * rpw + g;
+            float mk[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mk[i] = (i < per && li + lpr * i < W) ? lo_f(e[k][i]) : -INFINITY;
+            float M = fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3]));
+            M = group_max_dpp(M, lpr);
+            double S = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (mk[i] != -INFINITY) S += (double)hi_f(e[k][i]) * (double)__builtin_amdgcn_exp2f((mk[i] - M) * c);
+            S = group_sum_dpp(S, lpr);
+            if (ri < nrows && li == 0) {
+                const int r = stat_row(ri, N);
+                sM[r] = M;
+                sS[r] = S;
+            }
         }
     }
 }
 
-// Row r (storage index: q row u at u, p row c at N + c) carries an fp64 slice
-// sum from step 1.
-__device__ __forceinline__ bool row_has64(int r, int N, int all64, const int* par) {
-    return all64 || (r < N ? r == 0 : par[r - N] == 0);
-}
-
-// Merges the statistics of up to 2 rows per wave over the team: raw max, the
-// normaliser from the fp32 slice sums (assembled in fp64) and, where step 1
-// formed them, the exact fp64 normaliser.  Rows come from the LDS list mrow.
-__device__ void merge_rows(const int* mrow, int nm, const uint64_t* stats, const double* stats64, int W, int N,
-                           int all64, const int* par, double inv_t64, const double* tab, float* sM, double* sS,
-                           double* sS64) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int i0 = 2 * wave; i0 < nm; i0 += 2 * kWaves) {
-        uint64_t e[2][4];
-        double e64[2][4];
-        int rr[2];
-        bool h64[2];
+// Greedy: argmax of every target row 0..N-1 from stats[r][W].
+__device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W, int* amax) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lpr = lanes_per_row(W);
+    const int rpw = kWave / lpr;
+    const int per = (W + lpr - 1) / lpr;
+    const int g = lane / lpr, li = lane % lpr;
+    for (int r0 = wave * rpw * kBatch; r0 < N; r0 += kWaves * rpw * kBatch) {
+        uint64_t e[kBatch][4];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            rr[k] = mrow[min(i0 + k, nm - 1)];
-            h64[k] = (i0 + k < nm) && row_has64(rr[k], N, all64, par);
+        for (int k = 0; k < kBatch; ++k) {
+            const int r = min(r0 + k * rpw + g, N - 1);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = lane + kWave * q;
-                const bool ok = (i0 + k < nm) && j < W;
-                e[k][q] = ok ? ld_dev(&stats[(size_t)rr[k] * W + j]) : pack2(-INFINITY, 0.f);
-                e64[k][q] = (ok && h64[k]) ? ld_dev_d(&stats64[(size_t)rr[k] * W + j]) : 0.0;
-            }
+            for (int i = 0; i < 4; ++i) e[k][i] = ld_dev(&stats[(size_t)r * W + min(li + lpr * i, W - 1)]);
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (i0 + k >= nm) continue;
-            float m = -INFINITY;
+        for (int k = 0; k < kBatch; ++k) {
+            const int r = r0 + k * rpw + g;
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) m = fmaxf(m, lo_f(e[k][q]));
-            m = wave_max(m);
-            double s = 0.0, s64 = 0.0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float mj = lo_f(e[k][q]);
-                if (mj == -INFINITY) continue;
-                const double f = exp_scaled(mj, m, inv_t64, tab);
-                s += (double)hi_f(e[k][q]) * f;
-                s64 += e64[k][q] * f;
-            }
-            s = wave_sum_d(s);
-            s64 = wave_sum_d(s64);
-            if (lane == 0) {
-                sM[rr[k]] = m;
-                sS[rr[k]] = h64[k] ? s64 : s;
-                sS64[rr[k]] = h64[k] ? s64 : -1.0;
-            }
+            for (int i = 0; i < 4; ++i)
+                if (i < per && li + lpr * i < W) argmax_merge(bv, bi, lo_f(e[k][i]), __float_as_int(hi_f(e[k][i])));
+            group_argmax_dpp(bv, bi, lpr);
+            if (r < N && li == 0) amax[r] = bi;
         }
     }
+}
+
+// --------------------------------------------------------- residual passes --
+// Slice passes walk the slice in blocks of pass_vec<VEC4>() 4-element vectors
+// per thread; a block's loads are issued together (addresses clamped into the
+// slice), then its arithmetic runs under the per-element bounds.
+template <bool VEC4>
+__device__ constexpr int pass_vec() { return VEC4 ? 4 : 1; }
+
+template <bool VEC4>
+__device__ __forceinline__ f32x4 load_slice4(const float* row, int e, int nsl) {
+    f32x4 x;
+    if constexpr (VEC4) {
+        x = *reinterpret_cast<const f32x4*>(row + min(e, nsl - 4));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = row[min(e + k, nsl - 1)];
+    }
+    return x;
+}
+
+// One member's slice of w = max(0, R - P_c) into res[] (in place), with R the
+// target at u: softmax(q_u / T) (q row pointer given) or the stored residual
+// scaled by invZ.  Returns this thread's fp64 share of the slice mass; at `x2`
+// (slice-local, or -1) it reports the stored residual before the update (0 when
+// R was the target row) and the new one.
+template <bool VEC4>
+__device__ __forceinline__ double residual_pass(const float* qrow, const float* prow, float Mq, float invSq, float Mp,
+                                                float invSp, float invZ, float c, int nsl, float* res, int x2,
+                                                float* w_old, float* w_new) {
+    double part = 0.0;
+    const int n4 = (nsl + 3) / 4;
+    constexpr int kPassVec = pass_vec<VEC4>();
+    for (int base = 0; base < n4; base += kPassVec * kThreads) {
+        f32x4 xq[kPassVec], xp[kPassVec];
+#pragma unroll
+        for (int i = 0; i < kPassVec; ++i) {
+            const int e = 4 * (base + threadIdx.x + kThreads * i);
+            xp[i] = load_slice4<VEC4>(prow, e, nsl);
+            if (qrow) xq[i] = load_slice4<VEC4>(qrow, e, nsl);
+        }
+#pragma unroll
+        for (int i = 0; i < kPassVec; ++i) {
+            const int e4 = base + threadIdx.x + kThreads * i;
+            if (e4 >= n4) continue;
+            const int e = 4 * e4;
+            const f32x4 r = *reinterpret_cast<const f32x4*>(res + e);
+            f32x4 wv;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float rv = qrow ? __builtin_amdgcn_exp2f((xq[i][k] - Mq) * c) * invSq : r[k] * invZ;
+                const float pv = __builtin_amdgcn_exp2f((xp[i][k] - Mp) * c) * invSp;
+                const float w = (e + k < nsl && rv > pv) ? rv - pv : 0.f;
+                if (e + k == x2) {
+                    *w_old = qrow ? 0.f : r[k];
+                    *w_new = w;
+                }
+                wv[k] = w;
+                part += (double)w;
+            }
+            *reinterpret_cast<f32x4*>(res + e) = wv;
+        }
+    }
+    return part;
+}
+
+// softmax(q_u / T) of one slice, unnormalised: res[e] = exp((q - Mq) / T).
+template <bool VEC4>
+__device__ __forceinline__ void target_slice(const float* qrow, float Mq, float c, int nsl, float* res) {
+    const int n4 = (nsl + 3) / 4;
+    constexpr int kPassVec = pass_vec<VEC4>();
+    for (int base = 0; base < n4; base += kPassVec * kThreads) {
+        f32x4 xq[kPassVec];
+#pragma unroll
+        for (int i = 0; i < kPassVec; ++i) xq[i] = load_slice4<VEC4>(qrow, 4 * (base + threadIdx.x + kThreads * i), nsl);
+#pragma unroll
+        for (int i = 0; i < kPassVec; ++i) {
+            const int e4 = base + threadIdx.x + kThreads * i;
+            if (e4 >= n4) continue;
+            const int e = 4 * e4;
+            f32x4 wv;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) wv[k] = e + k < nsl ? __builtin_amdgcn_exp2f((xq[i][k] - Mq) * c) : 0.f;
+            *reinterpret_cast<f32x4*>(res + e) = wv;
+        }
+    }
+}
+
+// Inverse CDF within one member's slice: the first element e (ascending) whose
+// running fp64 sum exceeds tau with res[e] > 0; if none does (tau at or beyond
+// the slice total through rounding, or tau < 0 meaning "fallback"), the last
+// element with res[e] > 0.  Returns the slice-local index (or -1 if no mass).
+__device__ __forceinline__ int slice_draw(const float* res, int nsl, double tau, double* wt, int* s_tok) {
+    const int t = threadIdx.x;
+    const int run = (nsl + kThreads - 1) / kThreads;
+    const int a0 = min(nsl, t * run), a1 = min(nsl, a0 + run);
+    double sum = 0.0;
+    int lastp = -1;
+    for (int e = a0; e < a1; ++e) {
+        const float v = res[e];
+        sum += (double)v;
+        if (v > 0.f) lastp = e;
+    }
+    double excl, tot;
+    const double incl = block_scan_d(sum, wt, excl, tot);
+    if (t == 0) *s_tok = -1;
+    __syncthreads();
+    if (tau >= 0.0 && sum > 0.0 && excl <= tau && incl > tau) {
+        double cum = excl;
+        int tok = lastp;  // the run's total rounds above tau: its last element with mass
+        for (int e = a0; e < a1; ++e) {
+            const float v = res[e];
+            cum += (double)v;
+            if (v > 0.f && cum > tau) {
+                tok = e;
+                break;
+            }
+        }
+        *s_tok = tok;
+    }
+    __syncthreads();
+    int tok = *s_tok;
+    if (tok < 0) {
+        // fallback: the last element with mass
+        __syncthreads();
+        atomicMax(s_tok, lastp);
+        __syncthreads();
+        tok = *s_tok;
+    }
+    return tok;
 }
 
 // ---------------------------------------------------------------- the kernel --
 template <bool GREEDY, bool VEC4>
-__global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void spec_accept_kernel(const AccArgs a) {
+    const int tid = threadIdx.x;
     const int team = blockIdx.x / a.W;
     const int w = blockIdx.x % a.W;
     const int N = a.N, V = a.V, W = a.W;
     const int s0 = w * a.slice;
-    const int s1 = min(V, s0 + a.slice);
-    // each thread owns a contiguous run of the slice in the vocabulary passes
-    const int run = (s1 - s0 + kThreads - 1) / kThreads;
-    const int r0 = min(s1, s0 + tid * run);
-    const int r1 = min(s1, r0 + run);
-    const size_t rowsW = (size_t)2 * N * W;
-    uint64_t* stats_team = a.stats + (size_t)team * 2 * rowsW;
-    double* stats64_team = GREEDY ? nullptr : a.stats64 + (size_t)team * 2 * rowsW;
-    double* p64 = a.p64 + (size_t)team * 2 * kP64Slots * W;
-    double* rb = GREEDY ? nullptr : a.rbuf + (size_t)team * 2 * V;
+    const int nsl = min(V, s0 + a.slice) - s0;
+    const float c = a.c;
 
-    __shared__ int s_par[TV_MAX_NODES], s_draft[TV_MAX_NODES], s_amax[TV_MAX_NODES], s_depth[TV_MAX_NODES];
-    __shared__ int s_path[TV_MAX_NODES], s_mrow[TV_MAX_NODES + 1];
+    __shared__ int s_par[TV_MAX_NODES], s_draft[TV_MAX_NODES], s_path[TV_MAX_NODES], s_depth[TV_MAX_NODES];
+    __shared__ float s_gq[TV_MAX_NODES], s_gp[TV_MAX_NODES];
     __shared__ float s_M[2 * TV_MAX_NODES];
-    __shared__ double s_S[2 * TV_MAX_NODES], s_S64[2 * TV_MAX_NODES];
+    __shared__ double s_S[2 * TV_MAX_NODES];
+    // sampling: the member's slice of the current residual
+    __shared__ __attribute__((aligned(16))) float s_res[GREEDY ? 4 : kMaxSlice];
     __shared__ double s_wt[kWaves];
-    __shared__ double s_excl[kThreads];
+    __shared__ double s_mass[GREEDY ? 1 : kMaxTeamSize];
     __shared__ double s_tab[32];
-    __shared__ int s_ok, s_nm, s_hit[kWaves], s_last[kWaves], s_tok;
+    __shared__ double s_rejZ[GREEDY ? 1 : TV_MAX_NODES];
+    __shared__ int s_rej[GREEDY ? 1 : TV_MAX_NODES];
+    __shared__ float s_wx[2];
+    __shared__ double s_oexcl;
+    __shared__ int s_ok, s_last, s_tok, s_owner, s_fallback, s_hitw[kWaves], s_lastw[kWaves];
     __shared__ uint64_t s_base;
 
     if (tid < 32) exp2_table(s_tab, tid);
     TeamSync sync;
-    sync.line = a.ctrl + (size_t)team * kCtrlLine;
-    sync.arrive = a.arrive + (size_t)team * kMaxTeamSize;
+    sync.line = GREEDY ? nullptr : a.ctrl + (size_t)team * kCtrlLine;
+    sync.arrive = GREEDY ? nullptr : a.arrive + (size_t)team * kMaxTeamSize;
     sync.k = 0;
-    if (tid == 0) s_base = (ld_dev(&sync.line[0]) + 1) << kTagShift;
-    __syncthreads();
-    sync.base = s_base;
-    int phase = 0;  // parity of the fp64 publication slots
+    sync.base = 0;
+    uint64_t gen = 0;
+    if constexpr (!GREEDY) {
+        if (tid == 0) gen = ld_dev(&sync.line[0]);  // used at the first barrier; the load overlaps the stream
+    }
+    bool have_base = false;
 
     int iter = 0;
     for (int b = team; b < a.B; b += a.nteams, ++iter) {
-        // member 0 may still read the previous sequence's statistics while the
-        // others stream this one: alternate between two buffers
-        uint64_t* stats = stats_team + (size_t)(iter & 1) * rowsW;
-        double* stats64 = GREEDY ? nullptr : stats64_team + (size_t)(iter & 1) * rowsW;
-
         // ---- tree and drafts of this sequence ----
         if (tid < kWave) {
             int ok = 1;
@@ -425,50 +590,10 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             if (tid == 0) s_ok = all_ok;
         }
         __syncthreads();
-        const bool valid = s_ok;
-
-        // ---- 1. slice statistics of every row ----
-        const float* qb = a.q + (size_t)b * N * V;
-        const float* pb = GREEDY ? nullptr : a.p + (size_t)b * N * V;
-        const int nrows = valid ? (GREEDY ? N : 2 * N - 1) : 0;
-        for (int rs = wave * kRowsInFlight; rs < nrows; rs += kWaves * kRowsInFlight) {
-            const float* rows[kRowsInFlight];
-            bool want64[kRowsInFlight];
-            int srow[kRowsInFlight];
-            const int nr = min(kRowsInFlight, nrows - rs);
-#pragma unroll
-            for (int i = 0; i < kRowsInFlight; ++i) {
-                const int r = min(rs + i, nrows - 1);
-                const bool is_q = r < N;
-                srow[i] = is_q ? r : r + 1;  // p row c is stored at N + c
-                if constexpr (GREEDY) {
-                    rows[i] = qb + (size_t)r * V;  // greedy streams target rows only
-                    want64[i] = false;
-                } else {
-                    rows[i] = is_q ? qb + (size_t)r * V : pb + (size_t)(r - N + 1) * V;
-                    want64[i] = row_has64(srow[i], N, a.all64, s_par);
-                }
-            }
-            RowAcc acc[kRowsInFlight];
-            stream_rows<GREEDY, VEC4>(rows, want64, nr, s0, s1, lane, a.inv_t, a.inv_t64, s_tab, acc);
-            if (lane == 0) {
-#pragma unroll
-                for (int i = 0; i < kRowsInFlight; ++i) {
-                    if (i >= nr) continue;  // fully unrolled: the arrays stay in registers
-                    if constexpr (GREEDY) {
-                        st_dev(&stats[(size_t)srow[i] * W + w], pack2(acc[i].bv, __int_as_float(acc[i].bi)));
-                    } else {
-                        st_dev(&stats[(size_t)srow[i] * W + w], pack2(acc[i].m, acc[i].s));
-                        if (want64[i]) st_dev_d(&stats64[(size_t)srow[i] * W + w], acc[i].s64);
-                    }
-                }
-            }
-        }
-        team_sync(sync, w, W);
-
         int32_t* out_nodes = a.accepted + (size_t)b * N;
         int32_t* out_toks = a.tokens + (size_t)b * N;
-        if (!valid) {
+        if (!s_ok) {
+            // every member sees the same tree: nobody streams or synchronises
             if (w == 0) {
                 if (tid == 0) a.accept_len[b] = -1;
                 for (int i = tid; i < N; i += kThreads) {
@@ -480,265 +605,228 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             continue;
         }
 
+        const float* qb = a.q + (size_t)b * N * V;
+        const float* pb = GREEDY ? nullptr : a.p + (size_t)b * N * V;
+        // rows streamed: target rows 0..N-1, then (sampling) draft rows 1..N-1
+        const int nrows = GREEDY ? N : 2 * N - 1;
+        // gathered logits of the accept tests, in flight during the stream
+        float gq = 0.f, gp = 0.f;
+        const int gc = tid + 1;
+        if (!GREEDY && gc < N) {
+            const int x = s_draft[gc];
+            gq = qb[(size_t)s_par[gc] * V + x];
+            gp = pb[(size_t)gc * V + x];
+        }
+
+        // ---- 1. slice statistics of every row ----
+        uint64_t* stats = GREEDY ? a.stats + (size_t)b * N * W
+                                 : a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)2 * N * W;
+        stream_slices<GREEDY, VEC4>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w);
         if constexpr (GREEDY) {
-            if (w == 0) {
-                // member 0 merges the argmax of every target row (4 rows in
-                // flight per wave) and writes the path
-                for (int rq = wave; rq < N; rq += 4 * kWaves) {
-                    uint64_t e[4][4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int r = rq + kWaves * k, j = lane + kWave * q;
-                            e[k][q] = (r < N && j < W) ? ld_dev(&stats[(size_t)r * W + j])
-                                                       : pack2(-INFINITY, __int_as_float(0x7fffffff));
-                        }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int r = rq + kWaves * k;
-                        if (r >= N) continue;
-                        float bv = -INFINITY;
-                        int bi = 0x7fffffff;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) argmax_merge(bv, bi, lo_f(e[k][q]), __float_as_int(hi_f(e[k][q])));
-#pragma unroll
-                        for (int o = 32; o > 0; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o), __shfl_xor(bi, o));
-                        if (lane == 0) s_amax[r] = bi;
+            // ---- 2. the last member to publish merges and writes the path ----
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) {
+                const uint32_t prev =
+                    __hip_atomic_fetch_add(&a.counter[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_last = prev == (uint32_t)W - 1;
+                if (s_last) __hip_atomic_store(&a.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (!s_last) continue;
+            int* s_amax = s_path;  // reuse: argmax per target row
+            merge_greedy(stats, N, W, s_amax);
+            for (int i = tid; i < N; i += kThreads) {
+                out_nodes[i] = -1;
+                out_toks[i] = -1;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                // valid(i): every draft on the root-to-i path equals its parent's argmax
+                uint64_t ok = 1ull;
+                s_depth[0] = 0;
+                int e = 0;
+                for (int i = 1; i < N; ++i) {
+                    const int pr = s_par[i];
+                    s_depth[i] = s_depth[pr] + 1;
+                    if (((ok >> pr) & 1ull) && s_draft[i] == s_amax[pr]) {
+                        ok |= 1ull << i;
+                        if (s_depth[i] > s_depth[e]) e = i;
                     }
                 }
-                for (int i = tid; i < N; i += kThreads) {
-                    out_nodes[i] = -1;
-                    out_toks[i] = -1;
+                const int len = s_depth[e];
+                for (int i = e, k = len - 1; i != 0; i = s_par[i], --k) {
+                    out_nodes[k] = i;
+                    out_toks[k] = s_draft[i];
                 }
-                __syncthreads();
-                if (tid == 0) {
-                    // valid(i): every draft on the root-to-i path equals its parent's argmax
-                    uint64_t ok = 1ull;
-                    s_depth[0] = 0;
-                    int e = 0;
-                    for (int i = 1; i < N; ++i) {
-                        const int pr = s_par[i];
-                        s_depth[i] = s_depth[pr] + 1;
-                        if (((ok >> pr) & 1ull) && s_draft[i] == s_amax[pr]) {
-                            ok |= 1ull << i;
-                            if (s_depth[i] > s_depth[e]) e = i;
-                        }
-                    }
-                    const int len = s_depth[e];
-                    for (int i = e, k = len - 1; i != 0; i = s_par[i], --k) {
-                        out_nodes[k] = i;
-                        out_toks[k] = s_draft[i];
-                    }
-                    out_toks[len] = s_amax[e];
-                    a.accept_len[b] = len;
-                }
+                out_toks[len] = s_amax[e];
+                a.accept_len[b] = len;
             }
             __syncthreads();
         } else {
-            const double inv_t64 = a.inv_t64;
-            // merged statistics of node u's target row and its children's draft rows
-            auto visit = [&](int u) {
-                if (tid == 0) {
-                    int nm = 0;
-                    s_mrow[nm++] = u;
-                    for (int c = u + 1; c < N; ++c)
-                        if (s_par[c] == u) s_mrow[nm++] = N + c;
-                    s_nm = nm;
-                }
+            // ---- 3. barrier, then every member merges every row ----
+            if (!have_base) {
+                if (tid == 0) s_base = (gen + 1) << kTagShift;
                 __syncthreads();
-                merge_rows(s_mrow, s_nm, stats, stats64, W, N, a.all64, s_par, inv_t64, s_tab, s_M, s_S, s_S64);
-                __syncthreads();
-            };
+                sync.base = s_base;
+                have_base = true;
+            }
+            team_sync(sync, w, W);
+            if (gc < N) {
+                s_gq[gc] = gq;
+                s_gp[gc] = gp;
+            }
+            merge_sampling(stats, nrows, N, W, c, s_M, s_S);
+            __syncthreads();
 
-            // ---- 2./3. the walk (identical on every member) ----
-            int u = 0, len = 0, cur = 0;
-            bool res_active = false;  // target at u: residual rb[cur]/Z, else softmax(q_u / T)
-            bool masses_ready = false;  // the last residual pass left the draw's slice masses
-            double Z = 1.0, my_excl = 0.0, my_incl = 0.0, tsum = 0.0;
-            const double* mass_slot = nullptr;
-            for (int i = tid; i < 2 * N; i += kThreads) s_S64[i] = -1.0;  // no exact normaliser yet
-            visit(0);
-            int c = 1;
+            // ---- the walk (identical on every member) ----
+            const double inv_t64 = a.inv_t64;
+            double* massb = a.mass + (size_t)team * N * W * kMassRec;
+            int u = 0, len = 0, pass = 0, nrej = 0;
+            bool res_active = false;  // target at u: residual s_res / Z, else softmax(q_u / T)
+            double Z = 1.0, wx_cur = 0.0;
+            int c_cur = 1;
             for (;;) {
-                while (c < N && s_par[c] != u) ++c;
-                if (c >= N) break;  // every child of u tried, or u is a leaf
+                while (c_cur < N && s_par[c_cur] != u) ++c_cur;
+                if (c_cur >= N) break;  // every child of u tried, or u is a leaf
+                const int cc = c_cur;
                 {
-                    // accept test in fp64, the same on every member and thread
-                    const int x = s_draft[c];
-                    const double rx = res_active ? ld_dev_d(&rb[(size_t)cur * V + x]) / Z
-                                                 : exp_scaled(qb[(size_t)u * V + x], s_M[u], inv_t64, s_tab) / s_S[u];
-                    const double px = exp_scaled(pb[(size_t)c * V + x], s_M[N + c], inv_t64, s_tab) / s_S[N + c];
+                    const double rx = res_active ? wx_cur / Z
+                                                 : exp_scaled(s_gq[cc], s_M[u], inv_t64, s_tab) / s_S[u];
+                    const double px = exp_scaled(s_gp[cc], s_M[N + cc], inv_t64, s_tab) / s_S[N + cc];
                     const double acc = px == 0.0 ? 1.0 : fmin(1.0, rx / px);
-                    const double r = (double)philox_uniform(a.seed, (uint32_t)c, (uint32_t)b, 0u);
+                    const double r = (double)philox_uniform(a.seed, (uint32_t)cc, (uint32_t)b, 0u);
                     if (r < acc) {
-                        if (tid == 0) s_path[len] = c;
+                        if (tid == 0) s_path[len] = cc;
                         ++len;
-                        u = c;
-                        c = u + 1;
+                        u = cc;
+                        c_cur = u + 1;
                         res_active = false;
-                        masses_ready = false;
                         Z = 1.0;
-                        visit(u);
+                        nrej = 0;
                         continue;
                     }
                 }
-                // rejected: make sure the exact normalisers of q_u and p_c exist
-                const bool need_q = !res_active && s_S64[u] < 0.0;
-                const bool need_p = s_S64[N + c] < 0.0;
-                if (need_q || need_p) {
-                    double sq = 0.0, sp = 0.0;
-                    const float Mq = s_M[u], Mp = s_M[N + c];
-                    for (int v = s0 + tid; v < s1; v += kThreads) {
-                        if (need_q) sq += exp_scaled(qb[(size_t)u * V + v], Mq, inv_t64, s_tab);
-                        if (need_p) sp += exp_scaled(pb[(size_t)c * V + v], Mp, inv_t64, s_tab);
-                    }
-                    sq = block_sum_d(sq, s_wt);
-                    sp = block_sum_d(sp, s_wt);
-                    double* slot = p64 + (size_t)(phase & 1) * kP64Slots * W;
-                    if (tid == 0) {
-                        st_dev_d(&slot[w], sq);
-                        st_dev_d(&slot[W + w], sp);
-                    }
-                    team_sync(sync, w, W);
-                    sq = gather_sum(slot, W, s_wt);
-                    sp = gather_sum(slot + W, W, s_wt);
-                    ++phase;
-                    if (tid == 0) {
-                        if (need_q) s_S64[u] = sq;
-                        if (need_p) s_S64[N + c] = sp;
-                    }
-                    __syncthreads();
-                }
-                // next sibling, whose exact normaliser this pass forms as well
-                int nxt = c + 1;
+                // ---- 4. rejected: residual pass over the slices ----
+                int nxt = cc + 1;
                 while (nxt < N && s_par[nxt] != u) ++nxt;
-                const bool spec = nxt < N && s_S64[N + nxt] < 0.0;
-                {
-                    const float Mq = s_M[u], Mp = s_M[N + c];
-                    const float Mn = spec ? s_M[N + nxt] : 0.f;
-                    const double invSq = res_active ? 0.0 : 1.0 / s_S64[u];
-                    const double invSp = 1.0 / s_S64[N + c];
-                    const double invZ = 1.0 / Z;
-                    const double* src = rb + (size_t)cur * V;
-                    double* dst = rb + (size_t)(cur ^ 1) * V;
-                    double part = 0.0, pn = 0.0;
-                    for (int v = r0; v < r1; ++v) {
-                        const double rv = res_active ? ld_dev_d(&src[v]) * invZ
-                                                     : exp_scaled(qb[(size_t)u * V + v], Mq, inv_t64, s_tab) * invSq;
-                        const double pv = exp_scaled(pb[(size_t)c * V + v], Mp, inv_t64, s_tab) * invSp;
-                        const double wv = rv > pv ? rv - pv : 0.0;
-                        st_dev_d(&dst[v], wv);
-                        part += wv;
-                        if (spec) pn += exp_scaled(pb[(size_t)nxt * V + v], Mn, inv_t64, s_tab);
-                    }
-                    double slice_mass, excl;
-                    const double incl = block_scan_d(part, s_wt, excl, slice_mass);
-                    pn = block_sum_d(pn, s_wt);
-                    double* slot = p64 + (size_t)(phase & 1) * kP64Slots * W;
+                const int x2 = nxt < N ? s_draft[nxt] - s0 : -1;
+                const int x2l = (x2 >= 0 && x2 < nsl) ? x2 : -1;
+                if (tid == 0) {
+                    s_wx[0] = 0.f;
+                    s_wx[1] = 0.f;
+                }
+                __syncthreads();
+                const float Mq = s_M[u];
+                const float invSq = (float)(1.0 / s_S[u]);
+                const float invZ = (float)(1.0 / Z);
+                const float* q_u = qb + (size_t)u * V + s0;
+                const double part = residual_pass<VEC4>(res_active ? nullptr : q_u, pb + (size_t)cc * V + s0, Mq,
+                                                        invSq, s_M[N + cc], (float)(1.0 / s_S[N + cc]), invZ, c,
+                                                        nsl, s_res, x2l, &s_wx[1], &s_wx[0]);
+                const double smass = block_sum_d(part, s_wt);  // its barriers publish s_wx
+                double* slot = massb + (size_t)pass * W * kMassRec;
+                if (tid == 0) {
+                    st_dev_d(&slot[w * kMassRec + 0], smass);
+                    st_dev_d(&slot[w * kMassRec + 1], (double)s_wx[0]);  // new residual at the next token
+                    st_dev_d(&slot[w * kMassRec + 2], (double)s_wx[1]);  // stored residual before the pass
+                }
+                team_sync(sync, w, W);
+                // every member gathers the slice masses and the next sibling's residual
+                const double mt = tid < W ? ld_dev_d(&slot[tid * kMassRec + 0]) : 0.0;
+                const int xo = nxt < N ? s_draft[nxt] / a.slice : -1;
+                if (tid == xo) {
+                    s_wx[0] = (float)ld_dev_d(&slot[tid * kMassRec + 1]);
+                    s_wx[1] = (float)ld_dev_d(&slot[tid * kMassRec + 2]);
+                }
+                double mexcl, Znew;
+                block_scan_d(mt, s_wt, mexcl, Znew);  // its barriers publish s_wx too
+                ++pass;
+                if (Znew > 0.0) {
+                    if (tid < W) s_mass[tid] = mt;
                     if (tid == 0) {
-                        st_dev_d(&slot[w], slice_mass);
-                        st_dev_d(&slot[W + w], pn);
+                        s_rej[nrej] = cc;
+                        s_rejZ[nrej] = Znew;
                     }
-                    team_sync(sync, w, W);
-                    const double Znew = gather_sum(slot, W, s_wt);
-                    const double Sn = gather_sum(slot + W, W, s_wt);
-                    ++phase;
-                    if (spec && tid == 0) s_S64[N + nxt] = Sn;
+                    ++nrej;
+                    res_active = true;
+                    Z = Znew;
+                    wx_cur = (double)s_wx[0];
+                } else {
+                    // zero mass cannot follow a rejection in exact arithmetic: keep R.  The
+                    // slice was overwritten, so rebuild it from q_u and the earlier rejections.
+                    if (res_active) wx_cur = (double)s_wx[1];
                     __syncthreads();
-                    if (Znew > 0.0) {  // zero mass cannot follow a rejection in exact arithmetic: keep R then
-                        cur ^= 1;
-                        Z = Znew;
-                        res_active = true;
-                        // these slice masses and run sums serve the draw if no sibling follows
-                        masses_ready = true;
-                        mass_slot = slot;
-                        tsum = part;
-                        my_incl = incl;
-                        my_excl = excl;
+                    for (int k = 0; k < nrej; ++k) {
+                        const int ck = s_rej[k];
+                        const float iz = (float)(1.0 / (k == 0 ? 1.0 : s_rejZ[k - 1]));
+                        residual_pass<VEC4>(k == 0 ? q_u : nullptr, pb + (size_t)ck * V + s0, Mq, invSq,
+                                            s_M[N + ck], (float)(1.0 / s_S[N + ck]), iz, c, nsl, s_res, -1,
+                                            &s_wx[1], &s_wx[1]);
                     }
                 }
-                ++c;
+                __syncthreads();
+                c_cur = cc + 1;
             }
 
-            // ---- 4. the extra token: inverse CDF over the team's slices ----
+            // ---- 5. the extra token: inverse CDF over the slices ----
             const double ut = (double)philox_uniform(a.seed, (uint32_t)u, (uint32_t)b, 1u);
-            const float Mu = s_M[u];
-            const double* src = rb + (size_t)cur * V;
-            const float* qrow = qb + (size_t)u * V;
-            if (!masses_ready) {
-                // draw from softmax(q_u / T) (leaf bonus or residual kept unchanged):
-                // unnormalised weights exp((q - max)/T), masses per run and slice
-                tsum = 0.0;
-                for (int v = r0; v < r1; ++v)
-                    tsum += res_active ? ld_dev_d(&src[v]) : exp_scaled(qrow[v], Mu, inv_t64, s_tab);
-                double slice_mass;
-                my_incl = block_scan_d(tsum, s_wt, my_excl, slice_mass);
-                double* slot = p64 + (size_t)(phase & 1) * kP64Slots * W;
-                if (tid == 0) st_dev_d(&slot[w], slice_mass);
-                team_sync(sync, w, W);
-                ++phase;
-                mass_slot = slot;
+            // slice masses: of the last residual pass, or from the statistics when
+            // drawing from softmax(q_u / T)
+            double mt = 0.0;
+            if (tid < W) {
+                if (res_active) {
+                    mt = s_mass[tid];
+                } else {
+                    const uint64_t e = ld_dev(&stats[(size_t)u * W + tid]);
+                    mt = lo_f(e) == -INFINITY ? 0.0
+                                              : (double)hi_f(e) * (double)__builtin_amdgcn_exp2f((lo_f(e) - s_M[u]) * c);
+                }
             }
-            // every member finds the owner slice the same way: the first slice
-            // whose running mass exceeds U * total (the last slice with mass if
-            // rounding left the target at the total)
-            const double my_t = tid < W ? ld_dev_d(&mass_slot[tid]) : 0.0;
-            double total, slot_excl;
-            const double prefix = block_scan_d(my_t, s_wt, slot_excl, total);
-            s_excl[tid] = slot_excl;
+            double mexcl, total;
+            const double mincl = block_scan_d(mt, s_wt, mexcl, total);
             const double target = ut * total;
-            const bool has = tid < W && my_t > 0.0;
-            const uint64_t hit = __ballot(has && prefix > target);
-            const uint64_t pos = __ballot(has);
-            if (lane == 0) {
-                s_hit[wave] = hit ? wave * kWave + __ffsll((unsigned long long)hit) - 1 : -1;
-                s_last[wave] = pos ? wave * kWave + 63 - __clzll((unsigned long long)pos) : -1;
+            // owner: the first slice whose running mass exceeds the target; else the last with mass
+            {
+                const bool has = tid < W && mt > 0.0;
+                const uint64_t hit = __ballot(has && mincl > target);
+                const uint64_t pos = __ballot(has);
+                const int lane = tid & 63, wv = tid >> 6;
+                if (lane == 0) {
+                    s_hitw[wv] = hit ? wv * kWave + __ffsll((unsigned long long)hit) - 1 : -1;
+                    s_lastw[wv] = pos ? wv * kWave + 63 - __clzll((unsigned long long)pos) : -1;
+                }
+                __syncthreads();
+                if (tid == 0) {
+                    int owner = -1, lastm = -1;
+                    for (int k = 0; k < kWaves; ++k) {
+                        if (owner < 0) owner = s_hitw[k];
+                        lastm = max(lastm, s_lastw[k]);
+                    }
+                    s_fallback = owner < 0;
+                    s_owner = owner < 0 ? lastm : owner;
+                }
+                __syncthreads();
+                if (tid == s_owner) s_oexcl = mexcl;
+                __syncthreads();
             }
-            __syncthreads();
-            int owner = -1, last_pos = -1;
-            for (int i = 0; i < kWaves; ++i) {
-                if (owner < 0) owner = s_hit[i];
-                last_pos = max(last_pos, s_last[i]);
-            }
-            const bool fallback = owner < 0;
-            if (fallback) owner = last_pos;
-            const double before = owner >= 0 ? s_excl[owner] : 0.0;
+            const int owner = s_owner;
             if (w == owner) {
-                if (tid == 0) s_tok = -1;
+                if (!res_active) target_slice<VEC4>(qb + (size_t)u * V + s0, s_M[u], c, nsl, s_res);
                 __syncthreads();
-                const double tgt = target - before;
-                if (!fallback && my_excl <= tgt && my_incl > tgt && tsum > 0.0) {
-                    double cum = my_excl;
-                    int tok = -1, lastp = -1;
-                    for (int v = r0; v < r1; ++v) {
-                        const double wv = res_active ? ld_dev_d(&src[v]) : exp_scaled(qrow[v], Mu, inv_t64, s_tab);
-                        if (wv > 0.0) lastp = v;
-                        cum += wv;
-                        if (wv > 0.0 && cum > tgt) {
-                            tok = v;
-                            break;
-                        }
-                    }
-                    s_tok = tok >= 0 ? tok : lastp;
-                }
-                __syncthreads();
-                if (s_tok < 0 && tid == 0) {
-                    // target at or beyond the slice total (rounding), or fallback: last token with mass
-                    int tok = -1;
-                    for (int v = s1 - 1; v >= s0; --v) {
-                        const double wv = res_active ? ld_dev_d(&src[v]) : exp_scaled(qrow[v], Mu, inv_t64, s_tab);
-                        if (wv > 0.0) {
-                            tok = v;
-                            break;
-                        }
-                    }
-                    s_tok = tok >= 0 ? tok : s1 - 1;
-                }
-                __syncthreads();
+                const double tau = s_fallback ? -1.0 : target - s_oexcl;
+                int tok = slice_draw(s_res, nsl, tau, s_wt, &s_tok);
+                tok = tok < 0 ? nsl - 1 : tok;
                 for (int i = tid; i < N; i += kThreads) {
                     out_nodes[i] = i < len ? s_path[i] : -1;
-                    out_toks[i] = i < len ? s_draft[s_path[i]] : (i == len ? s_tok : -1);
+                    out_toks[i] = i < len ? s_draft[s_path[i]] : (i == len ? s0 + tok : -1);
+                }
+                if (tid == 0) a.accept_len[b] = len;
+            } else if (owner < 0 && w == 0) {
+                // no mass anywhere (only possible with non-finite logits): last token
+                for (int i = tid; i < N; i += kThreads) {
+                    out_nodes[i] = i < len ? s_path[i] : -1;
+                    out_toks[i] = i < len ? s_draft[s_path[i]] : (i == len ? V - 1 : -1);
                 }
                 if (tid == 0) a.accept_len[b] = len;
             }
@@ -797,14 +885,21 @@ int resident_capacity() {
     return cache[dev];
 }
 
-bool make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
+// 0 ok, else a tv_status.
+int make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
     const int cap = resident_capacity();
-    if (cap <= 0) return false;
+    if (cap <= 0) return TV_ERR_HIP;
     int wmax = (V + kMinSlice - 1) / kMinSlice;
     if (wmax > kMaxTeamSize) wmax = kMaxTeamSize;
+    // sampling keeps a member's residual slice in LDS
+    const int wmin = greedy ? 1 : (V + kMaxSlice - 1) / kMaxSlice;
+    if (wmin > kMaxTeamSize) return TV_ERR_UNSUPPORTED;
+    if (wmax < wmin) wmax = wmin;
     int W = cap / (B > 0 ? B : 1);
     if (W > wmax) W = wmax;
+    if (W < wmin) W = wmin;
     if (W < 1) W = 1;
+    if (W > cap) return TV_ERR_UNSUPPORTED;  // a team must be resident at once
     int slice = (V + W - 1) / W;
     slice = (slice + 3) / 4 * 4;
     W = (V + slice - 1) / slice;
@@ -817,19 +912,18 @@ bool make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
     pl.slice = slice;
     size_t off = 0;
     pl.ctrl_off = off;
-    off += round_up((size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t), 256);
+    if (!greedy) off += round_up((size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t), 256);
     pl.arrive_off = off;
-    off += round_up((size_t)kMaxTeams * kMaxTeamSize * sizeof(uint64_t), 256);
+    if (!greedy) off += round_up((size_t)kMaxTeams * kMaxTeamSize * sizeof(uint64_t), 256);
+    pl.counter_off = off;
+    if (greedy) off += round_up((size_t)B * sizeof(uint32_t), 256);
     pl.stats_off = off;
-    off += round_up((size_t)nteams * 2 * 2 * N * W * sizeof(uint64_t), 256);
-    pl.stats64_off = off;
-    if (!greedy) off += round_up((size_t)nteams * 2 * 2 * N * W * sizeof(double), 256);
-    pl.p64_off = off;
-    off += round_up((size_t)nteams * 2 * kP64Slots * W * sizeof(double), 256);
-    pl.rbuf_off = off;
-    if (!greedy) off += round_up((size_t)nteams * 2 * V * sizeof(double), 256);
+    off += greedy ? round_up((size_t)B * N * W * sizeof(uint64_t), 256)
+                  : round_up((size_t)nteams * 2 * 2 * N * W * sizeof(uint64_t), 256);
+    pl.mass_off = off;
+    if (!greedy) off += round_up((size_t)nteams * N * W * kMassRec * sizeof(double), 256);
     pl.total = off;
-    return true;
+    return TV_OK;
 }
 
 }  // namespace
@@ -838,7 +932,7 @@ bool make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
 extern "C" size_t tv_spec_accept_workspace(int B, int N, int V, int greedy) {
     if (B <= 0 || N < 1 || N > TV_MAX_NODES || V < 1) return 0;
     tv::AcceptPlan pl;
-    if (!tv::make_plan(B, N, V, greedy, pl)) return 0;
+    if (tv::make_plan(B, N, V, greedy, pl) != TV_OK) return 0;
     return pl.total;
 }
 
@@ -857,7 +951,8 @@ extern "C" int tv_spec_accept(const float* q_logits, const float* p_logits, cons
     if (!aligned(q_logits, 4) || (!greedy && !aligned(p_logits, 4))) return TV_ERR_INVALID_ARG;
     if (!workspace || !aligned(workspace, 256)) return TV_ERR_WORKSPACE;
     AcceptPlan pl;
-    if (!make_plan(B, N, V, greedy, pl)) return TV_ERR_HIP;
+    const int st = make_plan(B, N, V, greedy, pl);
+    if (st != TV_OK) return st;
     if (workspace_bytes < pl.total) return TV_ERR_WORKSPACE;
 
     char* ws = static_cast<char*>(workspace);
@@ -869,20 +964,18 @@ extern "C" int tv_spec_accept(const float* q_logits, const float* p_logits, cons
     a.accept_len = accept_len;
     a.accepted = accepted_nodes;
     a.tokens = out_tokens;
-    a.ctrl = reinterpret_cast<uint64_t*>(ws + pl.ctrl_off);
-    a.arrive = reinterpret_cast<uint64_t*>(ws + pl.arrive_off);
+    a.ctrl = greedy ? nullptr : reinterpret_cast<uint64_t*>(ws + pl.ctrl_off);
+    a.arrive = greedy ? nullptr : reinterpret_cast<uint64_t*>(ws + pl.arrive_off);
+    a.counter = greedy ? reinterpret_cast<uint32_t*>(ws + pl.counter_off) : nullptr;
     a.stats = reinterpret_cast<uint64_t*>(ws + pl.stats_off);
-    a.stats64 = greedy ? nullptr : reinterpret_cast<double*>(ws + pl.stats64_off);
-    a.p64 = reinterpret_cast<double*>(ws + pl.p64_off);
-    a.rbuf = greedy ? nullptr : reinterpret_cast<double*>(ws + pl.rbuf_off);
+    a.mass = greedy ? nullptr : reinterpret_cast<double*>(ws + pl.mass_off);
     a.B = B;
     a.N = N;
     a.V = V;
     a.W = pl.W;
     a.slice = pl.slice;
     a.nteams = pl.nteams;
-    a.all64 = !greedy && (long)B * (2 * N - 1) * V <= kSmallWork;
-    a.inv_t = greedy ? 1.f : (float)(1.0 / (double)temperature);
+    a.c = greedy ? 1.f : (float)(1.4426950408889634 / (double)temperature);
     a.inv_t64 = greedy ? 1.0 : 1.0 / (double)temperature;
     a.seed = philox_seed;
     const bool vec4 = (V % 4 == 0) && aligned(q_logits, 16) && (greedy || aligned(p_logits, 16));

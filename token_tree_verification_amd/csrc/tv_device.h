@@ -68,15 +68,102 @@ __host__ __device__ __forceinline__ double exp_nonpos(double y, const double* ta
 // tab[j] = 2^(j/32), j = 0..31 (from the library's exp2).
 __host__ __device__ __forceinline__ void exp2_table(double* tab, int j) { tab[j] = exp2((double)j / 32.0); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// ---- wave reductions on DPP lane moves (no LDS round trips) ----
+// quad_perm [1,0,3,2] and [2,3,0,1] combine the lanes of a quad, row_half_mirror
+// the two quads of each 8-lane half-row, row_mirror the two halves of each
+// 16-lane row; readlane then combines the four rows.  Every step pairs lanes
+// whose values are already uniform over the smaller group, so mirrors act as
+// xor exchanges.  All 64 lanes must be active.
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, true);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Reductions over aligned groups of `g` lanes (g a power of two, 1..64,
+// wave-uniform); every lane of a group receives the group's result.
+__device__ __forceinline__ float group_max_dpp(float v, int g) {
+    if (g >= 2) v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+    if (g >= 4) v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+    if (g >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    if (g >= 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+    if (g >= 32) {
+        const float r0 = readlane_f(v, 0), r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
+        const int lane = threadIdx.x & 63;
+        v = g == 64 ? fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)) : (lane < 32 ? fmaxf(r0, r1) : fmaxf(r2, r3));
+    }
     return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+__device__ __forceinline__ double group_sum_dpp(double v, int g) {
+    if (g >= 2) v += dpp_d<kDppQuadXor1>(v);
+    if (g >= 4) v += dpp_d<kDppQuadXor2>(v);
+    if (g >= 8) v += dpp_d<kDppHalfMirror>(v);
+    if (g >= 16) v += dpp_d<kDppRowMirror>(v);
+    if (g >= 32) {
+        const double r0 = readlane_d(v, 0), r1 = readlane_d(v, 16), r2 = readlane_d(v, 32), r3 = readlane_d(v, 48);
+        const int lane = threadIdx.x & 63;
+        v = g == 64 ? (r0 + r1) + (r2 + r3) : (lane < 32 ? r0 + r1 : r2 + r3);
+    }
     return v;
+}
+// (value, index) maximum: larger value wins, equal values go to the smaller index.
+__device__ __forceinline__ void argmax_step(float& v, int& i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+__device__ __forceinline__ void group_argmax_dpp(float& v, int& i, int g) {
+    if (g >= 2) argmax_step(v, i, dpp_f<kDppQuadXor1>(v), dpp_i<kDppQuadXor1>(i));
+    if (g >= 4) argmax_step(v, i, dpp_f<kDppQuadXor2>(v), dpp_i<kDppQuadXor2>(i));
+    if (g >= 8) argmax_step(v, i, dpp_f<kDppHalfMirror>(v), dpp_i<kDppHalfMirror>(i));
+    if (g >= 16) argmax_step(v, i, dpp_f<kDppRowMirror>(v), dpp_i<kDppRowMirror>(i));
+    if (g >= 32) {
+        float rv[4];
+        int ri[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            rv[k] = readlane_f(v, 16 * k);
+            ri[k] = __builtin_amdgcn_readlane(i, 16 * k);
+        }
+        const int lane = threadIdx.x & 63;
+        float a = rv[0], b = rv[2];
+        int ai = ri[0], bi = ri[2];
+        argmax_step(a, ai, rv[1], ri[1]);
+        argmax_step(b, bi, rv[3], ri[3]);
+        if (g == 64) {
+            argmax_step(a, ai, b, bi);
+            v = a;
+            i = ai;
+        } else {
+            v = lane < 32 ? a : b;
+            i = lane < 32 ? ai : bi;
+        }
+    }
 }
 
 }  // namespace tv
