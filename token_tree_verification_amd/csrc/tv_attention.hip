@@ -9,24 +9,32 @@
 //
 // Design (gfx950):
 //  * The G = Hq/Hkv query heads sharing a KV head and the N tree nodes are
-//    packed into R = G*N query rows per (sequence, KV head); a workgroup covers
-//    up to 8 blocks of 32 rows, so for grouped-query heads each K/V byte read
-//    from HBM serves every row of the group.
-//  * One wave owns 32 query rows.  Scores are computed transposed,
-//    S^T = K_tile . Q^T, with v_mfma_f32_32x32x16_bf16 (keys on the M side),
-//    so a lane holds scores of a single query row: max, sum and the rescale of
-//    the output accumulator are lane-local (one cross-half shuffle).
+//    packed into R = G*N query rows per (sequence, KV head).  A wave owns 64
+//    rows as two 32-row MFMA blocks; a workgroup's four waves form KG key
+//    groups of 4/KG row-waves, so one K/V byte read from HBM serves up to 256
+//    rows (grouped-query heads share it).
+//  * K and V tiles go from HBM straight to LDS (global_load_lds, 16 bytes per
+//    lane) into an S-stage ring per key group, S - 1 tiles ahead of the
+//    arithmetic.  Rows of 256 bytes are stored with their 16-byte chunks
+//    XOR-swizzled by twice the low key bits, so the K fragment reads (8 lanes
+//    per cycle) and the transposed V reads (16 lanes) hit distinct banks.
+//  * Scores are computed transposed, S^T = K . Q^T, with
+//    v_mfma_f32_32x32x16_bf16 (keys on the M side): a lane holds the scores of
+//    a single query row, so max, sum and the output rescale are lane-local
+//    (plus one cross-half exchange).  The K fragment read from LDS feeds both
+//    row blocks.
 //  * P.V runs as O^T = V^T . P^T with v_mfma_f32_32x32x16_f16: P is rounded to
-//    fp16 (bf16 P would cost ~1.5e-3 relative error), V is converted to fp16
-//    while it is staged, transposed, into LDS.  The score accumulator already
-//    holds P^T in B-operand order once the keys of each 16-key step are
-//    permuted; V^T is read with the same permutation.
+//    fp16 (bf16 P would cost ~1.5e-3 relative error).  V^T fragments come from
+//    the bf16 V tile with ds_read_b64_tr_b16 (each lane receives four keys at
+//    one head-dim position) and are converted to fp16 in registers; the
+//    score accumulator already holds P^T in B-operand order once the keys of
+//    each 16-key step are permuted, and the transposed reads use the same
+//    permutation.
 //  * Softmax in the exp2 domain with the scale folded into one FMA per score;
 //    the running max is raised lazily (only when a score exceeds it by more
 //    than 2^8), so most tiles skip the accumulator rescale; masks are applied
-//    only on tree tiles and the ragged last tile.
-//  * The next tile's global loads are issued before the current tile is
-//    computed (register prefetch), so HBM latency overlaps the MFMA work.
+//    only on tree tiles and the ragged last tile.  The exponentials of one row
+//    block are scheduled between the MFMAs of the other.
 //  * Tree keys are one or two extra tiles processed by the last KV split; the
 //    mask bit for (row, key j) is bit j of the row's 64-bit ancestor word,
 //    held in a register.
@@ -44,8 +52,14 @@ namespace tv {
 namespace {
 
 constexpr int HD = TV_HEAD_DIM;
-constexpr int kTargetWorkgroups = 1024;
-constexpr float kLazyThresh = 8.f;  // log2 units the running max may lag the true max
+constexpr int kThreads = 256;
+constexpr int kRowBytes = HD * 2;            // one key row of K or V (bf16)
+constexpr int kTargetWorkgroups = 256;   // one per CU (a workgroup fills a CU)
+constexpr int kBalance = 1;              // splits beyond kBalance * sqrt(L / R) are not worth their merge
+constexpr float kLazyThresh = 8.f;           // log2 units the running max may lag the true max
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct AttnArgs {
     const uint16_t* Q;
@@ -64,39 +78,43 @@ struct AttnArgs {
 };
 
 struct Plan {
-    int variant;  // 0: 1 row block x 4 key groups, 32-key tiles; 1: 2 x 2, 32; 2: 4 x 1, 64; 3: 8 x 1, 64
-    int R, rb, kg, kt, row_tiles, nsplit, tiles_per_split, cache_tiles, tree_tiles;
+    int variant;  // key groups x tile keys x stages x row blocks per wave: 4x32x2x1, 4x32x2x2, 2x64x2x2, 1x64x4x2
+    int kg, kt, rows, R, row_tiles, nsplit, tiles_per_split, cache_tiles, tree_tiles;
 };
 
 Plan make_plan(int B, int N, int Hq, int Hkv, int L) {
     Plan p;
     const int G = Hq / Hkv;
     p.R = G * N;
-    const int r32 = (p.R + 31) / 32;
-    if (r32 <= 1) {
-        p.variant = 0; p.rb = 1; p.kg = 4; p.kt = 32;
-    } else if (r32 <= 2) {
-        p.variant = 1; p.rb = 2; p.kg = 2; p.kt = 32;
-    } else if (r32 <= 4) {
-        p.variant = 2; p.rb = 4; p.kg = 1; p.kt = 64;
+    int rbw = 2;
+    if (p.R <= 32) {
+        p.variant = 0; p.kg = 4; p.kt = 32; rbw = 1;
+    } else if (p.R <= 64) {
+        p.variant = 1; p.kg = 4; p.kt = 32;
+    } else if (p.R <= 128) {
+        p.variant = 2; p.kg = 2; p.kt = 64;
     } else {
-        p.variant = 3; p.rb = 8; p.kg = 1; p.kt = 64;
+        p.variant = 3; p.kg = 1; p.kt = 64;
     }
-    p.row_tiles = (r32 + p.rb - 1) / p.rb;
+    p.rows = (4 / p.kg) * 32 * rbw;
+    p.row_tiles = (p.R + p.rows - 1) / p.rows;
     p.cache_tiles = (L + p.kt - 1) / p.kt;
     p.tree_tiles = (N + p.kt - 1) / p.kt;
     const long base = (long)B * Hkv * p.row_tiles;
     int nsplit = 1;
     p.tiles_per_split = 0;
     if (p.cache_tiles > 0) {
+        // enough workgroups for one per CU, but the last workgroup of a group
+        // merges nsplit partials of R rows while each split streams L / nsplit
+        // keys: beyond about sqrt(L / R) splits the merge costs more than it saves
         const long want = (kTargetWorkgroups + base - 1) / base;
-        const int max_split = (p.cache_tiles + 2 * p.kg - 1) / (2 * p.kg);  // at least two tiles per key group
+        int balance = 1;
+        while ((long)(balance + 1) * (balance + 1) * p.R <= (long)kBalance * kBalance * L) ++balance;
+        const int max_split = (p.cache_tiles + p.kg - 1) / p.kg;  // at least one tile per key group
         nsplit = (int)(want < max_split ? want : max_split);
+        if (nsplit > balance) nsplit = balance;
         if (nsplit < 1) nsplit = 1;
-        // the merging workgroup keeps one weight per (row, split) in the tile LDS
-        const int tile_lds = p.kg * (p.kt * (2 * TV_HEAD_DIM + 16) + TV_HEAD_DIM * (2 * p.kt + 8));
-        const int cap = tile_lds / (p.rb * 32 * 8);
-        if (nsplit > cap) nsplit = cap;
+        if (nsplit > 64) nsplit = 64;  // the merging workgroup keeps one weight per (row, split) in LDS
         int tps = (p.cache_tiles + nsplit - 1) / nsplit;
         tps = (tps + p.kg - 1) / p.kg * p.kg;
         p.tiles_per_split = tps;
@@ -114,7 +132,7 @@ WsLayout workspace_layout(int B, int Hkv, const Plan& p) {
     WsLayout w{0, 0, 0, 0};
     if (p.nsplit <= 1) return w;
     const size_t groups = (size_t)B * Hkv * p.row_tiles;
-    const size_t rows = groups * p.nsplit * p.rb * 32;
+    const size_t rows = groups * p.nsplit * p.rows;
     w.counter_off = 0;
     w.part_o_off = round_up(groups * sizeof(uint32_t), 256);
     w.part_ml_off = w.part_o_off + round_up(rows * HD * sizeof(float), 256);
@@ -152,30 +170,79 @@ __device__ __forceinline__ float ld_dev_f(const float* p) {
                                              __HIP_MEMORY_SCOPE_AGENT));
 }
 
-template <int RB, int KG, int KT>
-__global__ __launch_bounds__(64 * RB * KG) void tree_attention_kernel(const AttnArgs a) {
-    constexpr int NT = 64 * RB * KG;        // threads
-    constexpr int TPK = 64 * RB;            // threads per key group
-    constexpr int KB = KT / 32;             // 32-key MFMA blocks per tile
-    constexpr int K_STRIDE = HD * 2 + 16;   // LDS bytes per key row of the bf16 K tile
-    constexpr int V_STRIDE = KT * 2 + 8;    // LDS bytes per d row of the fp16 V^T tile (8-byte rows)
-    constexpr int K_BYTES = KT * K_STRIDE;
-    constexpr int V_BYTES = HD * V_STRIDE;
-    constexpr int BUF = (K_BYTES + V_BYTES + 15) / 16 * 16;
-    constexpr int KCH = KT * 16 / TPK;      // 16-byte K chunks per thread per tile
-    constexpr int VUN = KT * 8 / TPK;       // V units (2 keys x 8 d) per thread per tile
-    constexpr int O_STRIDE = HD + 4;        // floats per row of a key-group merge slot
-    constexpr int SLOT = 32 * O_STRIDE * 4 + 64 * 4;
-    static_assert(KCH >= 1 && VUN >= 1, "tile too small for the key group");
-    static_assert(KG == 1 || (KG - 1) * RB * SLOT <= KG * BUF, "merge slots must fit in the tile LDS");
-    __shared__ __attribute__((aligned(16))) char lds[KG * BUF];
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their maxima, i.e. not waited for).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane i writes
+// lds_addr + 16 i.  Issued as inline assembly so that the compiler does not
+// treat every later LDS read as dependent on it (it would wait for the whole
+// ring); completion is tracked explicitly with wait_vmcnt.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved but only this copy writes it
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS accesses by byte address (32-bit, address space 3).
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ u32x4 lds_ld128(uint32_t addr) { return *(const lds_u32x4*)(uintptr_t)addr; }
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)addr));
+}
+
+
+// bf16 bits -> fp16, two values per dword (exact for normal fp16 magnitudes).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    const float a = __uint_as_float(w << 16), b = __uint_as_float(w & 0xffff0000u);
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+// Max over the two halves of the wave (lanes l and l ^ 32 hold one query row).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int KG, int KT, int S, int RBW>
+__global__ __launch_bounds__(kThreads) void tree_attention_kernel(const AttnArgs a) {
+    constexpr int RW = 4 / KG;                     // row-waves per key group
+    constexpr int WROWS = RBW * 32;                // rows per wave
+    constexpr int ROWS = RW * WROWS;               // rows per workgroup
+    constexpr bool CONV_LDS = RW > 1;              // V converted to fp16 once per tile in LDS
+    constexpr int KB = KT / 32;                    // 32-key MFMA blocks per tile
+    constexpr int TILE = KT * kRowBytes;           // bytes of a K (or V) tile
+    constexpr int STAGE = 2 * TILE;                // K then V
+    constexpr int RING = S * STAGE;                // one key group's ring
+    constexpr int DMA = KT * kRowBytes / (16 * kWave) / RW;  // 16-byte DMA instructions per wave per operand
+    constexpr int O_STRIDE = HD + 4;               // floats per row of a key-group merge slot (conflict-free)
+    constexpr int DPW = HD / KG;                   // head dims each key group merges
+    static_assert(DMA >= 1, "tile too small for the key group");
+    constexpr int MERGE = KG > 1 ? KG * ROWS * (O_STRIDE + 2) * 4 : 0;  // key-group merge slots
+    constexpr int LDS_BYTES = KG * RING > MERGE ? KG * RING : MERGE;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];  // rows 256-byte aligned
     __shared__ int s_last;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int rb = wave % RB;
-    const int kg = wave / RB;
-    const int n = lane & 31;   // MFMA column: query row within the block / key within a 32-key block
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kg = wave / RW;
+    const int rw = wave % RW;
+    const int n = lane & 31;   // MFMA column: query row within a block / key within a 32-key block
     const int hf = lane >> 5;  // which half of the k-slots this lane carries
 
     const int logical = xcd_remap(blockIdx.x, a.nblocks);
@@ -187,21 +254,25 @@ __global__ __launch_bounds__(64 * RB * KG) void tree_attention_kernel(const Attn
     const int g = bg % a.Hkv;
     const float c = a.scale_log2;
 
-    // ---- the query row this lane carries as a B-operand column ----
-    const int r = (rt * RB + rb) * 32 + n;
-    const bool row_ok = r < a.R;
-    const int node = row_ok ? r / a.G : 0;
-    const int head = g * a.G + (row_ok ? r % a.G : 0);
-    bf16x8 qf[8];
-    {
+    // ---- the query rows this lane carries as B-operand columns ----
+    int row[RBW];
+    bool row_ok[RBW];
+    bf16x8 qf[RBW][8];
+    uint64_t anc_row[RBW];
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+        row[j] = rt * ROWS + rw * WROWS + 32 * j + n;
+        row_ok[j] = row[j] < a.R;
+        const int node = row_ok[j] ? row[j] / a.G : 0;
+        const int head = g * a.G + (row_ok[j] ? row[j] % a.G : 0);
         const uint16_t* qrow = a.Q + ((size_t)(b * a.N + node) * a.Hq + head) * HD;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf) : u32x4{0, 0, 0, 0};
-            qf[s] = __builtin_bit_cast(bf16x8, v);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
+            qf[j][s] = __builtin_bit_cast(bf16x8, row_ok[j] ? v : u32x4{0, 0, 0, 0});
         }
+        anc_row[j] = row_ok[j] ? a.anc[(size_t)b * a.N + node] : 0ull;
     }
-    const uint64_t anc_row = row_ok ? a.anc[(size_t)b * a.N + node] : 0ull;
 
     // ---- tiles of this workgroup: cache tiles of the split, then tree tiles ----
     const int t_begin = split * a.tiles_per_split;
@@ -211,15 +282,18 @@ __global__ __launch_bounds__(64 * RB * KG) void tree_attention_kernel(const Attn
     const int n_tree = (split == a.nsplit - 1) ? a.tree_tiles : 0;
     const int n_tiles = n_cache + n_tree;
     const int iters = (n_tiles + KG - 1) / KG;
+    char* ring = lds + kg * RING;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)(lds_void*)ring;
 
-    char* k_lds = lds + kg * BUF;
-    char* v_lds = k_lds + K_BYTES;
-    const int tk = rb * 64 + lane;  // thread index within the key group
-
-    // global source of tile k_idx (cache or tree) and its valid key count
-    auto tile_src = [&](int k_idx, const uint16_t*& ks, const uint16_t*& vs, size_t& stride, int& key0, int& nk,
-                        bool& is_tree) {
-        is_tree = k_idx >= n_cache;
+    // Issue this wave's share of the DMA of tile t (this key group's t-th
+    // tile, index k_idx = t * KG + kg) into stage st.
+    auto issue_tile = [&](int t, int st) {
+        const int k_idx = t * KG + kg;
+        if (k_idx >= n_tiles) return;  // uniform: nothing to load
+        const bool is_tree = k_idx >= n_cache;
+        int key0, nk;
+        const uint16_t *ks, *vs;
+        size_t stride;
         if (!is_tree) {
             key0 = (t_begin + k_idx) * KT;
             nk = min(KT, a.L - key0);
@@ -235,221 +309,311 @@ __global__ __launch_bounds__(64 * RB * KG) void tree_attention_kernel(const Attn
             vs = a.Vt + base;
             stride = (size_t)a.Hkv * HD;
         }
-    };
-
-    // register stage of one tile: KCH K chunks, VUN V units (2 keys each)
-    u32x4 kreg[KCH], vreg[VUN][2];
-    auto load_tile = [&](int k_idx) {
-        const uint16_t *ks, *vs;
-        size_t stride;
-        int key0, nk;
-        bool is_tree;
-        tile_src(k_idx, ks, vs, stride, key0, nk, is_tree);
+        const uint32_t kdst_addr = ring_addr + st * STAGE;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int ch = tk + TPK * i, key = ch >> 4, dc = ch & 15;
-            kreg[i] = key < nk ? *reinterpret_cast<const u32x4*>(ks + key * stride + dc * 8) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < VUN; ++i) {
-            const int un = tk + TPK * i, kp = un >> 4, dc = un & 15;
-            const int k0 = 2 * kp;
-            vreg[i][0] = k0 < nk ? *reinterpret_cast<const u32x4*>(vs + k0 * stride + dc * 8) : u32x4{0, 0, 0, 0};
-            vreg[i][1] = k0 + 1 < nk ? *reinterpret_cast<const u32x4*>(vs + (k0 + 1) * stride + dc * 8)
-                                     : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int ch = tk + TPK * i, key = ch >> 4, dc = ch & 15;
-            *reinterpret_cast<u32x4*>(k_lds + key * K_STRIDE + dc * 16) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VUN; ++i) {
-            const int un = tk + TPK * i, kp = un >> 4, dc = un & 15;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // V^T[d][2kp], V^T[d][2kp+1] as one fp16 pair, d = 8 dc + j
-                const uint32_t w0 = vreg[i][0][j >> 1], w1 = vreg[i][1][j >> 1];
-                const uint32_t h0 = (j & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-                const uint32_t h1 = (j & 1) ? (w1 >> 16) : (w1 & 0xffffu);
-                const _Float16 f0 = (_Float16)bf16_bits_to_float(h0);
-                const _Float16 f1 = (_Float16)bf16_bits_to_float(h1);
-                const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, f0) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, f1) << 16);
-                *reinterpret_cast<uint32_t*>(v_lds + (dc * 8 + j) * V_STRIDE + kp * 4) = pk;
-            }
+        for (int i = 0; i < DMA; ++i) {
+            const int inst = rw * DMA + i;          // 1 KB block of the tile
+            const int p = inst * kWave + lane;      // 16-byte chunk written by this lane
+            const int key = p >> 4, pc = p & 15;
+            const int lc = pc ^ (2 * (key & 7));    // logical chunk stored at physical chunk pc
+            const size_t off = (size_t)min(key, nk - 1) * stride + lc * 8;  // ragged keys repeat a valid row
+            dma16(ks + off, kdst_addr + inst * 1024);
+            dma16(vs + off, kdst_addr + TILE + inst * 1024);
         }
     };
 
-    f32x16 o_acc[4];
+    f32x16 o_acc[RBW][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o_acc[i] = f32x16{};
-    float m_used = -INFINITY, l_run = 0.f;  // m_used in raw score units
+    for (int j = 0; j < RBW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o_acc[j][i] = f32x16{};
+    float m_used[RBW], l_run[RBW];  // m_used in raw score units
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+        m_used[j] = -INFINITY;
+        l_run[j] = 0.f;
+    }
 
-    if (kg < n_tiles) load_tile(kg);
+    // prologue: the first S - 1 tiles of every key group
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) issue_tile(t, t);
+
+    // tiles of this key group
+    const int ntk = kg < n_tiles ? (n_tiles - kg + KG - 1) / KG : 0;
     for (int it = 0; it < iters; ++it) {
+        // tile `it` of this key group has landed: wait until at most the DMA of
+        // the later tiles already issued (up to S - 2 of them) is outstanding
+        const int later = min(S - 2, ntk - 1 - it);
+        if (later <= 0) {
+            wait_vmcnt<0>();
+        } else if constexpr (S > 2) {
+            if (later == 1) wait_vmcnt<2 * DMA>();
+            else wait_vmcnt<(S - 2) * 2 * DMA>();
+            static_assert(S <= 4, "wait counts cover rings of up to four stages");
+        }
+        __syncthreads();  // every wave's part is in LDS; the stage refilled below is free
+        issue_tile(it + S - 1, (it + S - 1) % S);
         const int k_idx = it * KG + kg;
-        const bool active = k_idx < n_tiles;
-        if (it > 0) __syncthreads();  // the previous tile is consumed by every wave
-        if (active) store_tile();
-        __syncthreads();
-        if (active && k_idx + KG < n_tiles) load_tile(k_idx + KG);  // in flight during the compute below
-        if (active) {
-            const uint16_t *ks_, *vs_;
-            size_t st_;
-            int key0, nk;
-            bool is_tree;
-            tile_src(k_idx, ks_, vs_, st_, key0, nk, is_tree);
-            const bool masked = is_tree || nk < KT;
-            // S^T[key][row] for KB blocks of 32 keys
-            f32x16 s_acc[KB];
+        const char* kt = ring + (it % S) * STAGE;
+        const char* vt = kt + TILE;
+        // V of this tile to fp16 in place, shared by the key group's row-waves
+        // (a single row-wave converts its fragments in registers instead)
+        if (CONV_LDS && k_idx < n_tiles) {
+            constexpr int CH = TILE / 16 / (RW * kWave);  // 16-byte chunks per lane
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                s_acc[kb] = f32x16{};
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const bf16x8 kf = __builtin_bit_cast(
-                        bf16x8,
-                        *reinterpret_cast<const u32x4*>(k_lds + (32 * kb + n) * K_STRIDE + (16 * s + 8 * hf) * 2));
-                    s_acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s_acc[kb], 0, 0, 0);
-                }
+            for (int i = 0; i < CH; ++i) {
+                u32x4* ch = reinterpret_cast<u32x4*>(const_cast<char*>(vt)) + (rw * CH + i) * kWave + lane;
+                const u32x4 x = *ch;
+                *ch = u32x4{bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]),
+                            bf16x2_to_f16x2(x[3])};
             }
-            // element e of block kb is key 32 kb + 8 (e/4) + 4 hf + (e%4) of the tile
+        }
+        if constexpr (CONV_LDS) __syncthreads();  // the converted V is visible to every row-wave
+        if (k_idx >= n_tiles) continue;  // uniform per wave
+        const bool is_tree = k_idx >= n_cache;
+        const int key0 = is_tree ? (k_idx - n_cache) * KT : (t_begin + k_idx) * KT;
+        const int nk = is_tree ? min(KT, a.N - key0) : min(KT, a.L - key0);
+        const bool masked = is_tree || nk < KT;
+
+        // LDS byte addresses.  Rows are 256-byte aligned; logical chunk c of
+        // key row k sits at chunk c ^ 2 (k & 7), so a chunk index can be XORed
+        // into bits 4..7 of a row address.
+        //  K fragment (kb, s): key 32 kb + n, logical chunk 2s + hf, stored at
+        //  2 (s ^ (n & 7)) + hf: address = (k_base ^ (s << 5)) + 8192 kb.
+        const uint32_t kt_addr = (uint32_t)(uintptr_t)(lds_void*)kt;
+        const uint32_t k_base = (kt_addr + n * kRowBytes + hf * 16) ^ ((n & 7) << 5);
+        //  V^T fragment of 16-key step t, head-dim block blk: lane (n, hf) gets
+        //  V[keys 16t + 4hf + 0..3 and 16t + 8 + 4hf + 0..3][32 blk + n].  For a
+        //  transposed read, the 16 lanes of group gq supply rows r = 0..3 (lanes
+        //  4r..4r+3, four head-dim values each) and receive one column each:
+        //  lane supplies key 16t + kr (+8), head dims d0 .. d0+3 with
+        //  kr = 4 (gq >> 1) + (w16 >> 2), d0 = 32 blk + 16 (gq & 1) + 4 (w16 & 3).
+        //  Its chunk d0 / 8 = 4 blk + c0 is stored at (4 blk + c0) ^ 2 kr (the
+        //  same for key + 8), so with v_base = row kr | ((c0 ^ 2 kr) << 4) |
+        //  byte (d0 & 7) * 2: lo address = (v_base ^ (blk << 6)) + 4096 t, hi =
+        //  lo + 2048 (eight rows further).
+        const int gq = lane >> 4, w16 = lane & 15;
+        const int kr = 4 * (gq >> 1) + (w16 >> 2);
+        const int c0 = 2 * (gq & 1) + ((w16 & 3) >> 1);
+        const uint32_t v_base =
+            ((kt_addr + TILE + kr * kRowBytes) | ((c0 ^ (2 * kr)) << 4)) + 8 * (w16 & 1);
+        uint32_t v_blk[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) v_blk[blk] = v_base ^ (blk << 6);
+
+        // the tile is processed in blocks of 32 keys (online softmax per block)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            // ---- S^T[key][row] for this block and the wave's row blocks ----
+            f32x16 s_acc[RBW];
+#pragma unroll
+            for (int j = 0; j < RBW; ++j) s_acc[j] = f32x16{};
+            bf16x8 kf[8];  // the block's K fragments, all reads in flight before the MFMAs
+#pragma unroll
+            for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(bf16x8, lds_ld128((k_base ^ (s << 5)) + 8192 * kb));
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int j = 0; j < RBW; ++j)
+                    s_acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[j][s], s_acc[j], 0, 0, 0);
+            // element e is key 32 kb + 8 (e/4) + 4 hf + (e%4) of the tile
             if (masked) {
+                const int kbase = 32 * kb;
+                const uint32_t ragged = nk - kbase >= 32 ? 0xffffffffu
+                                                         : (nk - kbase <= 0 ? 0u : (1u << (nk - kbase)) - 1u);
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                for (int j = 0; j < RBW; ++j) {
+                    uint32_t vis = ragged;
+                    if (is_tree) vis &= (uint32_t)(anc_row[j] >> ((key0 + kbase) & 63));
+                    vis >>= 4 * hf;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int key = 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
-                        bool vis = key < nk;
-                        if (is_tree) vis = vis && ((anc_row >> ((key0 + key) & 63)) & 1ull);
-                        if (!vis) s_acc[kb][e] = -INFINITY;
+                    for (int e = 0; e < 16; ++e)
+                        if (!((vis >> (8 * (e >> 2) + (e & 3))) & 1u)) s_acc[j][e] = -INFINITY;
+                }
+            }
+            // ---- running max: raised only when a score runs more than 2^8 above it ----
+            float mc[RBW];
+#pragma unroll
+            for (int j = 0; j < RBW; ++j) {
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s_acc[j][e]);
+                tmax = halves_max(tmax);
+                const bool raise = tmax > m_used[j] + kLazyThresh / c || m_used[j] == -INFINITY;
+                if (__ballot(raise)) {
+                    const float m_new = raise ? fmaxf(m_used[j], tmax) : m_used[j];
+                    const float alpha =
+                        (m_used[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used[j] - m_new) * c);
+                    if (raise) {
+                        l_run[j] *= alpha;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o_acc[j][i] *= alpha;
                     }
-            }
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s_acc[kb][e]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            // raise the running max only when a score runs more than 2^8 above it
-            const bool raise = tmax > m_used + kLazyThresh / c || m_used == -INFINITY;
-            if (__ballot(raise)) {
-                const float m_new = raise ? fmaxf(m_used, tmax) : m_used;
-                const float alpha = (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * c);
-                if (raise) {
-                    l_run *= alpha;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o_acc[i] *= alpha;
+                    m_used[j] = m_new;
                 }
-                m_used = m_new;
+                mc[j] = (m_used[j] == -INFINITY) ? 0.f : m_used[j] * c;
             }
-            const float mc = (m_used == -INFINITY) ? 0.f : m_used * c;
-            f16x8 pf[2 * KB];
-            float lsum = 0.f;
+            // ---- per 16-key step: P = exp2(s c - m c) as fp16 B operands, V^T
+            // fragments, O^T += V^T P^T.  Step h holds accumulator elements
+            // 8h .. 8h + 7 (keys in the permuted order above).
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int h = 0; h < 2; ++h) {
+                u32x4 pf[RBW];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s_acc[kb][e], c, -mc));
-                    lsum += p;
-                    pf[2 * kb + (e >> 3)][e & 7] = (_Float16)p;
+                for (int j = 0; j < RBW; ++j) {
+                    uint32_t w[4];
+                    float ls = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s_acc[j][8 * h + 2 * q], c, -mc[j]));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s_acc[j][8 * h + 2 * q + 1], c, -mc[j]));
+                        ls += p0 + p1;
+                        w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p0) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p1) << 16);
+                    }
+                    l_run[j] += ls;
+                    pf[j] = u32x4{w[0], w[1], w[2], w[3]};
                 }
-            l_run += lsum;
-            // O^T[d][row] += V^T[d][key] P^T[key][row]
-#pragma unroll
-            for (int t = 0; t < 2 * KB; ++t) {
+                const int t = 2 * kb + h;
+                u32x2 vl[4], vh[4];  // the step's V^T fragments, all reads in flight before the MFMAs
 #pragma unroll
                 for (int blk = 0; blk < 4; ++blk) {
-                    const char* vrow = v_lds + (32 * blk + n) * V_STRIDE + (16 * t + 4 * hf) * 2;
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-                    const f16x8 vf = __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                    o_acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[t], o_acc[blk], 0, 0, 0);
+                    vl[blk] = lds_tr16(v_blk[blk] + 4096 * t);
+                    vh[blk] = lds_tr16(v_blk[blk] + 4096 * t + 2048);
+                }
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk) {
+                    const u32x2 l2 = vl[blk], h2 = vh[blk];
+                    f16x8 vf;
+                    if constexpr (CONV_LDS) {
+                        vf = __builtin_bit_cast(f16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+                    } else {
+                        vf = __builtin_bit_cast(f16x8, u32x4{bf16x2_to_f16x2(l2.x), bf16x2_to_f16x2(l2.y),
+                                                             bf16x2_to_f16x2(h2.x), bf16x2_to_f16x2(h2.y)});
+                    }
+#pragma unroll
+                    for (int j = 0; j < RBW; ++j)
+                        o_acc[j][blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, __builtin_bit_cast(f16x8, pf[j]),
+                                                                               o_acc[j][blk], 0, 0, 0);
                 }
             }
         }
     }
 
-    float l_tot = l_run + __shfl_xor(l_run, 32);
-    float m_log = (m_used == -INFINITY) ? -INFINITY : m_used * c;  // log2 units from here on
+    float l_tot[RBW], m_log[RBW];
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+        l_tot[j] = halves_sum(l_run[j]);
+        m_log[j] = (m_used[j] == -INFINITY) ? -INFINITY : m_used[j] * c;  // log2 units from here on
+    }
 
-    // ---- merge the key groups of each row block through LDS ----
-    if constexpr (KG > 1) {
-        __syncthreads();
-        if (kg > 0) {
-            float* so = reinterpret_cast<float*>(lds + ((kg - 1) * RB + rb) * SLOT);
-            float* sml = so + 32 * O_STRIDE;
+    // ---- results per row: a lane holds head dims [d_lo, d_lo + DOUT) of row
+    // r_out (workgroup-relative), unnormalised, with its (m, l) ----
+    //  KG == 1: the MFMA layout itself (DOUT = 4-float pieces scattered); the
+    //  merged path below gathers rows instead.
+    const int grp = bg * a.row_tiles + rt;
+    const int row0 = rt * ROWS;
+    const int nrows = min(ROWS, a.R - row0);
+
+    if constexpr (KG == 1) {
+        if (a.nsplit == 1) {
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<f32x4*>(so + n * O_STRIDE + 32 * blk + 8 * j + 4 * hf) =
-                        f32x4{o_acc[blk][4 * j], o_acc[blk][4 * j + 1], o_acc[blk][4 * j + 2], o_acc[blk][4 * j + 3]};
-            if (hf == 0) {
-                sml[n] = m_log;
-                sml[32 + n] = l_tot;
-            }
-        }
-        __syncthreads();
-        if (kg == 0) {
-#pragma unroll
-            for (int k = 1; k < KG; ++k) {
-                const float* so = reinterpret_cast<const float*>(lds + ((k - 1) * RB + rb) * SLOT);
-                const float* sml = so + 32 * O_STRIDE;
-                const float mk = sml[n], lk = sml[32 + n];
-                const float M = fmaxf(m_log, mk);
-                const float a0 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_log - M);
-                const float ak = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+            for (int j = 0; j < RBW; ++j) {
+                if (!row_ok[j]) continue;
+                const int node = row[j] / a.G, head = g * a.G + row[j] % a.G;
+                const float inv = 1.f / l_tot[j];
+                float* dst = a.out + ((size_t)(b * a.N + node) * a.Hq + head) * HD;
 #pragma unroll
                 for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const f32x4 ov = *reinterpret_cast<const f32x4*>(so + n * O_STRIDE + 32 * blk + 8 * j + 4 * hf);
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<f32x4*>(dst + 32 * blk + 8 * q + 4 * hf) =
+                            f32x4{o_acc[j][blk][4 * q] * inv, o_acc[j][blk][4 * q + 1] * inv,
+                                  o_acc[j][blk][4 * q + 2] * inv, o_acc[j][blk][4 * q + 3] * inv};
+            }
+            return;
+        }
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) o_acc[blk][4 * j + q] = o_acc[blk][4 * j + q] * a0 + ov[q] * ak;
-                    }
-                l_tot = l_tot * a0 + lk * ak;
-                m_log = M;
+        for (int j = 0; j < RBW; ++j) {
+            if (!row_ok[j]) continue;
+            const size_t prow = ((size_t)grp * a.nsplit + split) * ROWS + (row[j] - row0);
+            float* dst = a.part_o + prow * HD;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    st_dev_f4(dst + 32 * blk + 8 * q + 4 * hf,
+                              f32x4{o_acc[j][blk][4 * q], o_acc[j][blk][4 * q + 1], o_acc[j][blk][4 * q + 2],
+                                    o_acc[j][blk][4 * q + 3]});
+            if (hf == 0) {
+                st_dev_f(a.part_ml + prow * 2, m_log[j]);
+                st_dev_f(a.part_ml + prow * 2 + 1, l_tot[j]);
             }
         }
-    }
-
-    if (a.nsplit == 1) {
-        if (kg != 0 || !row_ok) return;
-        const float inv = 1.f / l_tot;
-        float* dst = a.out + ((size_t)(b * a.N + node) * a.Hq + head) * HD;
+    } else {
+        // ---- merge the key groups through LDS, every wave taking DPW head dims ----
+        wait_vmcnt<0>();
+        __syncthreads();  // the ring is free
+        float* slots = reinterpret_cast<float*>(lds);                      // [KG][ROWS][O_STRIDE]
+        float* mls = slots + (size_t)KG * ROWS * O_STRIDE;                  // [KG][ROWS][2]
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
+        for (int j = 0; j < RBW; ++j) {
+            const int rr = rw * WROWS + 32 * j + n;  // workgroup-relative row
+            float* so = slots + ((size_t)kg * ROWS + rr) * O_STRIDE;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<f32x4*>(dst + 32 * blk + 8 * j + 4 * hf) =
-                    f32x4{o_acc[blk][4 * j] * inv, o_acc[blk][4 * j + 1] * inv, o_acc[blk][4 * j + 2] * inv,
-                          o_acc[blk][4 * j + 3] * inv};
-        return;
-    }
-
-    // ---- split-KV: publish this split's partial; the last workgroup merges ----
-    constexpr int RBR = RB * 32;                   // rows per row tile
-    const int grp = bg * a.row_tiles + rt;
-    const int row0 = rt * RBR;
-    const int nrows = min(RBR, a.R - row0);
-    if (kg == 0 && row_ok) {
-        const size_t prow = ((size_t)grp * a.nsplit + split) * RBR + (r - row0);
-        float* dst = a.part_o + prow * HD;
+            for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                st_dev_f4(dst + 32 * blk + 8 * j + 4 * hf,
-                          f32x4{o_acc[blk][4 * j], o_acc[blk][4 * j + 1], o_acc[blk][4 * j + 2], o_acc[blk][4 * j + 3]});
-        if (hf == 0) {
-            st_dev_f(a.part_ml + prow * 2, m_log);
-            st_dev_f(a.part_ml + prow * 2 + 1, l_tot);
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<f32x4*>(so + 32 * blk + 8 * q + 4 * hf) =
+                        f32x4{o_acc[j][blk][4 * q], o_acc[j][blk][4 * q + 1], o_acc[j][blk][4 * q + 2],
+                              o_acc[j][blk][4 * q + 3]};
+            if (hf == 0) {
+                mls[((size_t)kg * ROWS + rr) * 2] = m_log[j];
+                mls[((size_t)kg * ROWS + rr) * 2 + 1] = l_tot[j];
+            }
         }
+        __syncthreads();
+        // wave w merges head dims [DPW * (w % KG), + DPW) of rows (w / KG) + 4/KG * i:
+        // lanes hold rows, each lane DPW contiguous head dims
+        const int d_lo = DPW * (wave % KG);
+        for (int rr = wave / KG * kWave + lane; rr < ROWS; rr += RW * kWave) {
+            if (rr >= nrows) break;
+            float M = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < KG; ++k) M = fmaxf(M, mls[((size_t)k * ROWS + rr) * 2]);
+            float wk[KG], Lsum = 0.f;
+#pragma unroll
+            for (int k = 0; k < KG; ++k) {
+                const float mk = mls[((size_t)k * ROWS + rr) * 2];
+                wk[k] = (M == -INFINITY || mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+                Lsum += wk[k] * mls[((size_t)k * ROWS + rr) * 2 + 1];
+            }
+            const int grow = row0 + rr;
+            const int node = grow / a.G, head = g * a.G + grow % a.G;
+            const float inv = 1.f / Lsum;
+            const size_t prow = ((size_t)grp * a.nsplit + split) * ROWS + rr;
+#pragma unroll
+            for (int d4 = 0; d4 < DPW / 4; ++d4) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < KG; ++k)
+                    acc += wk[k] * *reinterpret_cast<const f32x4*>(slots + ((size_t)k * ROWS + rr) * O_STRIDE + d_lo +
+                                                                   4 * d4);
+                if (a.nsplit == 1)
+                    *reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.N + node) * a.Hq + head) * HD + d_lo + 4 * d4) =
+                        acc * inv;
+                else
+                    st_dev_f4(a.part_o + prow * HD + d_lo + 4 * d4, acc);
+            }
+            if (a.nsplit > 1 && wave % KG == 0) {
+                st_dev_f(a.part_ml + prow * 2, M);
+                st_dev_f(a.part_ml + prow * 2 + 1, Lsum);
+            }
+        }
+        if (a.nsplit == 1) return;
     }
+
+    // ---- split-KV: the partials are published; the last workgroup merges ----
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have landed
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -461,38 +625,71 @@ __global__ __launch_bounds__(64 * RB * KG) void tree_attention_kernel(const Attn
     if (!s_last) return;
 
     // last workgroup of the group: per row, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s
-    float* wts = reinterpret_cast<float*>(lds);  // [nrows][nsplit] (m_s, then the weight)
-    float* lsv = wts + nrows * a.nsplit;          // [nrows][nsplit] l_s
-    const size_t pbase = (size_t)grp * a.nsplit * RBR;
-    for (int e = threadIdx.x; e < nrows * a.nsplit; e += NT) {
-        const int i = e / a.nsplit, s = e % a.nsplit;
-        const float* ml = a.part_ml + (pbase + (size_t)s * RBR + i) * 2;
-        wts[e] = ld_dev_f(ml);
-        lsv[e] = ld_dev_f(ml + 1);
+    const int ns = a.nsplit;
+    float* wts = reinterpret_cast<float*>(lds);  // [nrows][ns] (m_s, then the weight)
+    float* lsv = wts + nrows * ns;               // [nrows][ns] l_s
+    const size_t pbase = (size_t)grp * ns * ROWS;
+    for (int e0 = 0; e0 < nrows * ns; e0 += 8 * kThreads) {
+        float mv[8], lv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = min(e0 + k * kThreads + (int)threadIdx.x, nrows * ns - 1);
+            const float* ml = a.part_ml + (pbase + (size_t)(e % ns) * ROWS + e / ns) * 2;
+            mv[k] = ld_dev_f(ml);
+            lv[k] = ld_dev_f(ml + 1);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = e0 + k * kThreads + (int)threadIdx.x;
+            if (e < nrows * ns) {
+                wts[e] = mv[k];
+                lsv[e] = lv[k];
+            }
+        }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nrows; i += NT) {
+    for (int i = threadIdx.x; i < nrows; i += kThreads) {
         float M = -INFINITY;
-        for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, wts[i * a.nsplit + s]);
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, wts[i * ns + s]);
         float Lsum = 0.f;
-        for (int s = 0; s < a.nsplit; ++s) {
-            const float wv = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wts[i * a.nsplit + s] - M);
-            wts[i * a.nsplit + s] = wv;
-            Lsum += wv * lsv[i * a.nsplit + s];
+        for (int s = 0; s < ns; ++s) {
+            const float wv = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wts[i * ns + s] - M);
+            wts[i * ns + s] = wv;
+            Lsum += wv * lsv[i * ns + s];
         }
         const float inv = 1.f / Lsum;
-        for (int s = 0; s < a.nsplit; ++s) wts[i * a.nsplit + s] *= inv;
+        for (int s = 0; s < ns; ++s) wts[i * ns + s] *= inv;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < nrows * (HD / 4); e += NT) {
-        const int i = e / (HD / 4), d4 = e % (HD / 4);
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int s = 0; s < a.nsplit; ++s)
-            acc += wts[i * a.nsplit + s] * ld_dev_f4(a.part_o + (pbase + (size_t)s * RBR + i) * HD + 4 * d4);
-        const int rr = row0 + i;
-        const int nd = rr / a.G, hd = g * a.G + rr % a.G;
-        *reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.N + nd) * a.Hq + hd) * HD + 4 * d4) = acc;
+    // each thread owns output float4s, two at a time, with 16 split loads in flight
+    const int nout = nrows * (HD / 4);
+    for (int e0 = threadIdx.x; e0 < nout; e0 += 2 * kThreads) {
+        int ei[2];
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int s0 = 0; s0 < ns; s0 += 8) {
+            f32x4 v[2][8];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                ei[u] = min(e0 + u * kThreads, nout - 1);
+                const float* src = a.part_o + (pbase + ei[u] / (HD / 4)) * HD + 4 * (ei[u] % (HD / 4));
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[u][k] = ld_dev_f4(src + (size_t)min(s0 + k, ns - 1) * ROWS * HD);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (s0 + k < ns) acc[u] += wts[(ei[u] / (HD / 4)) * ns + s0 + k] * v[u][k];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = e0 + u * kThreads;
+            if (e >= nout) continue;
+            const int i = e / (HD / 4), d4 = e % (HD / 4);
+            const int rr = row0 + i;
+            const int nd = rr / a.G, hd = g * a.G + rr % a.G;
+            *reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.N + nd) * a.Hq + hd) * HD + 4 * d4) = acc[u];
+        }
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&a.counter[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
@@ -560,16 +757,16 @@ extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, con
     hipStream_t st = (hipStream_t)stream;
     switch (p.variant) {
         case 0:
-            hipLaunchKernelGGL((tree_attention_kernel<1, 4, 32>), dim3(a.nblocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((tree_attention_kernel<4, 32, 2, 1>), dim3(a.nblocks), dim3(kThreads), 0, st, a);
             break;
         case 1:
-            hipLaunchKernelGGL((tree_attention_kernel<2, 2, 32>), dim3(a.nblocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((tree_attention_kernel<4, 32, 2, 2>), dim3(a.nblocks), dim3(kThreads), 0, st, a);
             break;
         case 2:
-            hipLaunchKernelGGL((tree_attention_kernel<4, 1, 64>), dim3(a.nblocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((tree_attention_kernel<2, 64, 2, 2>), dim3(a.nblocks), dim3(kThreads), 0, st, a);
             break;
         default:
-            hipLaunchKernelGGL((tree_attention_kernel<8, 1, 64>), dim3(a.nblocks), dim3(512), 0, st, a);
+            hipLaunchKernelGGL((tree_attention_kernel<1, 64, 4, 2>), dim3(a.nblocks), dim3(kThreads), 0, st, a);
             break;
     }
     return launch_status();
