@@ -22,6 +22,10 @@ HIPCC_FLAGS = [
     "-Wno-unused-result",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in architectural VGPRs: with the default AGPR form the
+    # loop-carried attention accumulators are copied between the two register
+    # files on every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
@@ -29,18 +33,46 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+# Extra flags per source.  The attention kernels compare MFMA results that are
+# never NaN: without NaN semantics a max is one v_max3 instead of a quieting
+# v_max per operand.
+FILE_FLAGS = {
+    "tv_attention.hip": ["-fno-honor-nans"],
+}
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into token_tree_verification_amd/libtv.so."""
+    """Compile every HIP source and link them into token_tree_verification_amd/libtv.so."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = ["hipcc", *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="tv_build_") as d:
+        def compile_one(src):
+            obj = os.path.join(d, os.path.basename(src) + ".o")
+            cmd = ["hipcc", *compile_flags, *FILE_FLAGS.get(os.path.basename(src), []), "-I", INCLUDE, "-I", CSRC,
+                   "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+        with ThreadPoolExecutor(max_workers=4) as ex:
+            results = list(ex.map(compile_one, sources()))
+        objs = []
+        for obj, res in results:
+            err = "\n".join(l for l in (res.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+            objs.append(obj)
+        cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{res.stderr}")
     os.replace(tmp, LIB)
     return LIB
 
