@@ -239,24 +239,40 @@ def test_accept_workspace_sizes(tv):
     # sampling keeps each member's residual slice on chip: no vocabulary-sized rows in the workspace
     assert s < 4 << 20
     # vocabularies whose slices cannot fit a team's on-chip residual are refused
-    assert tv.accept_workspace_bytes(1, 6, 256 * 8192 + 1, False) == 0
+    assert tv.accept_workspace_bytes(1, 6, 256 * 32768 + 1, False) == 0
 
 
 def test_accept_reuses_workspace_across_calls(tv):
     """The team barrier words live in the workspace and are never cleared:
-    repeated calls on one workspace must all match the oracle."""
+    repeated calls on one workspace, of either mode and of different shapes,
+    must all match the oracle."""
     w = CONFIGS["c2"]
     q, p, draft, parent_t = accept_inputs(w, device=dev())
-    qn, pn, dn, parn = _np(q), _np(p), _np(draft), _np(parent_t)
-    ws = torch.zeros(max(tv.accept_workspace_bytes(1, 6, 128256, False), 1 << 20), dtype=torch.uint8, device=dev())
+    w1 = CONFIGS["c1"]
+    q1, p1, d1, par1 = accept_inputs(w1, device=dev())
+    cases = [(q, p, draft, parent_t), (q1, p1, d1, par1)]
+    host = [tuple(_np(x) for x in c) for c in cases]
+    need = max(tv.accept_workspace_bytes(x.shape[0], x.shape[1], x.shape[2], g) for x, *_ in cases for g in (0, 1))
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     for seed in range(12):
         a, n, t = tv.spec_accept(q, p, draft, parent_t, seed=seed, temperature=1.0, workspace=ws)
         torch.cuda.synchronize()
-        ref = oracle.spec_accept(qn, pn, dn, parn, seed=seed, temperature=1.0)
+        ref = oracle.spec_accept(*host[0], seed=seed, temperature=1.0)
         _compare_walk((_np(a), _np(n), _np(t)), ref, False)
-    # team 0's control line: [0] generation (one per call), [2] barrier time-out flag
+    calls = 12
+    for seed in range(3):
+        for greedy in (True, False):
+            for (cq, cp, cd, cpar), (hq, hp, hd, hpar) in zip(cases, host):
+                a, n, t = tv.spec_accept(cq, None if greedy else cp, cd, cpar, seed=seed, temperature=1.0,
+                                         greedy=greedy, workspace=ws)
+                torch.cuda.synchronize()
+                ref = oracle.spec_accept(hq, hp, hd, hpar, seed=seed, temperature=1.0, greedy=greedy)
+                _compare_walk((_np(a), _np(n), _np(t)), ref, greedy)
+                calls += 1
+    # team 0's control line: [0] generation (one per call, either mode), [2]
+    # barrier time-out flag
     ctrl = _np(ws[:128].view(torch.int64))
-    assert ctrl[0] == 12 and ctrl[2] == 0
+    assert ctrl[0] == calls and ctrl[2] == 0
 
 
 def test_accept_edge_cases(tv):

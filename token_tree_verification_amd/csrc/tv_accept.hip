@@ -8,17 +8,18 @@
 // greedy verification keeps drafts equal to the target's greedy choice;
 // token-tree verification checks every candidate path and stays lossless.
 //
-// One launch.  A team of W workgroups owns one sequence at a time; member w
-// owns vocabulary slice w of every logit row.
+// One launch of one 1024-thread workgroup per CU (no co-resident workgroups
+// competing for a CU's bandwidth).  A team of W workgroups owns one sequence
+// at a time; member w owns vocabulary slice w of every logit row.
 //  1. Statistics: each member streams its slice of every row once (coalesced
-//     16-byte loads, prefetched a group ahead, every row's slice spread over
-//     the four waves) and publishes the slice max and sum of
+//     16-byte loads, prefetched a group ahead; its sixteen waves take rows
+//     from an LDS counter) and publishes the slice max and sum of
 //     exp((x - max)/T) -- or the max and its first index in greedy mode.
 //     The logits the walk tests, q_parent(c)(x_c) and p_c(x_c), are gathered
 //     while the stream is in flight.
-//  2. Greedy: the last member to publish (arrival counter per sequence) merges
-//     the argmax of every target row and writes the path; nobody waits.
-//  3. Sampling: one team barrier, then every member merges the statistics of
+//  2. A team barrier; greedy: member 0 merges the argmax of every target row
+//     and writes the path.
+//  3. Sampling: every member merges the statistics of
 //     every row and runs the same walk redundantly: decisions need only the
 //     merged statistics and the gathered logits, so all members agree bit for
 //     bit without communicating.
@@ -35,13 +36,14 @@
 // the gathered logits.  Decisions can differ from exact arithmetic only within
 // ~1e-6 of a boundary.
 //
-// Team barrier: members store a generation-tagged arrival word, member 0
-// gathers them and stores one release word.  Data crossing members goes
-// through device-scope loads and stores (coherent across XCDs without L2
-// write-back or invalidation); a member waits for its own stores to land
-// before it arrives.  Tags grow monotonically per team across calls (member 0
-// advances the team's generation word at the first barrier of a call), so the
-// control words never need clearing after the workspace was zero-filled once.
+// Team barrier: every member stores a generation-tagged arrival word and polls
+// the words of all the others (no relay through one member).  Data crossing
+// members goes through device-scope loads and stores (coherent across XCDs
+// without L2 write-back or invalidation); a member waits for its own stores
+// to land before it arrives.  Tags grow monotonically per team across calls
+// (member 0 advances the team's generation word once the first barrier of a
+// call has gathered everyone), so the control words never need clearing
+// after the workspace was zero-filled once.
 // The grid never exceeds the device's resident capacity, so all members of a
 // team run together; spins are bounded.
 #include <float.h>
@@ -54,22 +56,24 @@
 namespace tv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;       // one workgroup per CU: no co-resident workgroups competing for its bandwidth
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxTeamSize = 256;
 constexpr int kMaxTeams = 1024;
 constexpr int kMinSlice = 1024;      // logits per member and row, at least
-constexpr int kMaxSlice = 8192;      // sampling: a member's residual slice lives in LDS (32 KB)
+constexpr int kMaxSlice = 32768;     // sampling: a member's residual slice lives in LDS (128 KB)
+constexpr int kMaxSpans = 4095;      // greedy: spans of 256 logits per slice, at most
 constexpr int kSpan = 4 * kWave;     // logits one wave covers with one 16-byte load per lane
 constexpr int kGroup = 4;            // spans per prefetch group (two groups in flight per wave)
-constexpr int kCtrlLine = 16;        // u64 words per team: [0] generation, [1] release, [2] time-out flag
+constexpr int kCtrlLine = 16;        // u64 words per team: [0] generation, [2] time-out flag
 constexpr int kTagShift = 24;        // barrier tag = (generation << 24) + barrier index
 constexpr uint32_t kSpinLimit = 1u << 20;
-constexpr int kMassRec = 4;          // doubles per (pass, member): mass, new and old residual at the next token
+constexpr int kMassRec = 4;          // tagged u64 words per (pass, member): mass (two halves), new and old
+                                     // residual at the next token
 
 struct AcceptPlan {
     int W, nteams, slice;
-    size_t ctrl_off, arrive_off, counter_off, stats_off, mass_off, total;
+    size_t ctrl_off, arrive_off, stats_off, mass_off, total;
 };
 
 struct AccArgs {
@@ -80,10 +84,9 @@ struct AccArgs {
     int32_t* accept_len;
     int32_t* accepted;
     int32_t* tokens;
-    uint64_t* ctrl;      // sampling: [kMaxTeams][kCtrlLine]
-    uint64_t* arrive;    // sampling: [kMaxTeams][kMaxTeamSize]
-    uint32_t* counter;   // greedy: [B] arrivals per sequence, reset by the last arriver
-    uint64_t* stats;     // sampling: [nteams][2][2N][W] (max, sum); greedy: [B][N][W] (max, index)
+    uint64_t* ctrl;      // [kMaxTeams][kCtrlLine]
+    uint64_t* arrive;    // [kMaxTeams][kMaxTeamSize]
+    uint64_t* stats;     // [nteams][2][2N][W] (max, sum); greedy [nteams][2][N][W] (max, index)
     double* mass;        // sampling: [nteams][N][W][kMassRec]
     int B, N, V, W, slice, nteams;
     float c;             // log2(e) / T
@@ -97,12 +100,6 @@ __device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
 }
 __device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
     return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev_d(double* p, double v) {
-    st_dev(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v));
-}
-__device__ __forceinline__ double ld_dev_d(const double* p) {
-    return __longlong_as_double((long long)ld_dev(reinterpret_cast<const uint64_t*>(p)));
 }
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
     return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
@@ -122,27 +119,11 @@ __device__ __forceinline__ void team_sync(TeamSync& s, int w, int W) {
     const uint64_t tag = s.base + s.k;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's device-scope stores have landed
     __syncthreads();
-    if (w == 0) {
-        const int t = threadIdx.x;
-        if (t > 0 && t < W) {
-            uint32_t spins = 0;
-            while (ld_dev(&s.arrive[t]) < tag) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++spins > kSpinLimit) {
-                    st_dev(&s.line[2], 1ull);
-                    break;
-                }
-            }
-        }
-        __syncthreads();
-        if (t == 0) {
-            if (s.k == 1) st_dev(&s.line[0], s.base >> kTagShift);  // the next call starts after this generation
-            st_dev(&s.line[1], tag);
-        }
-    } else if (threadIdx.x == 0) {
-        st_dev(&s.arrive[w], tag);
+    const int t = threadIdx.x;
+    if (t == 0) st_dev(&s.arrive[w], tag);
+    if (t < W && t != w) {  // every member watches every other member's word
         uint32_t spins = 0;
-        while (ld_dev(&s.line[1]) < tag) {
+        while (ld_dev(&s.arrive[t]) < tag) {
             __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
                 st_dev(&s.line[2], 1ull);
@@ -151,6 +132,37 @@ __device__ __forceinline__ void team_sync(TeamSync& s, int w, int W) {
         }
     }
     __syncthreads();
+    // every member has read the generation word by now (before its first
+    // arrival): the next call starts after this generation
+    if (s.k == 1 && w == 0 && t == 0) st_dev(&s.line[0], s.base >> kTagShift);
+}
+
+// Walk steps exchange tagged words instead of passing a barrier: the tag is
+// (generation << 12 | step) in the upper 32 bits of every 64-bit word, so a
+// word from an earlier step, or from an earlier call, is told apart (a slot
+// would have to go unused for 2^20 calls and then be reused at the same step
+// to be mistaken).  Steps count on with the team's barrier index.
+__device__ __forceinline__ uint32_t exchange_tag(TeamSync& s) {
+    ++s.k;
+    return (uint32_t)(((s.base >> kTagShift) << 12) | (s.k & 0xfffu));
+}
+// Poll one member's kMassRec words until all carry tag `tg` (upper half).
+__device__ __forceinline__ void gather_tagged(TeamSync& s, const uint64_t* src, uint64_t tg, uint64_t* e) {
+    uint32_t spins = 0;
+    for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < kMassRec; ++i) {
+            e[i] = ld_dev(&src[i]);
+            ok = ok && (e[i] & 0xffffffff00000000ull) == tg;
+        }
+        if (ok) return;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+            st_dev(&s.line[2], 1ull);
+            return;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ helpers --
@@ -209,58 +221,79 @@ __device__ __forceinline__ const float* row_ptr(const float* qb, const float* pb
 }
 
 // ------------------------------------------------------- 1. statistics pass --
-// Wave k streams rows k, k + 4, ... (storage order: target rows, then draft
-// rows) over this member's slice, one 16-byte load per lane per span, a
-// prefetch group ahead of the arithmetic, and publishes each row's slice
-// statistics as soon as the row ends: sampling (max, sum of exp((x - max) c),
-// accumulated in fp64, stored as fp32), greedy (max, first index).
+// The workgroup streams its slice of every row (storage order: target rows,
+// then draft rows); its sixteen waves take rows one at a time from an LDS
+// counter, so a wave that gets less of the CU's issue bandwidth takes fewer
+// rows.  A row is streamed with one 16-byte load per lane per span of 256
+// logits, a prefetch group ahead of the arithmetic (across row boundaries);
+// every loaded span carries a tag (row << 12 | span, bit 31 on the row's last
+// span) and the row's slice statistics are published when its last span is
+// processed: sampling (max, sum of exp((x - max) c), accumulated in fp64,
+// stored as fp32), greedy (max, first index).
 template <bool GREEDY, bool VEC4>
 __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, int nrows, int N, int V, int s0,
-                                              int nsl, float c, uint64_t* stats, int W, int w) {
+                                              int nsl, float c, uint64_t* stats, int W, int w, int* rowctr) {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nspan = (nsl + kSpan - 1) / kSpan;
-    const int myrows = wave < nrows ? (nrows - wave + kWaves - 1) / kWaves : 0;
-    if (myrows == 0) return;
-
-    // Load cursor (row lr of this wave, span lj) and process cursor (pr, pj).
-    // Loads are unconditional so that several stay in flight: past the last
-    // item the cursor stays on it, and lanes past the slice end read its last
-    // vector and then see -inf.
-    int lr = 0, lj = 0, pr = 0, pj = 0;
-    const int last_lr = myrows - 1, last_lj = nspan - 1;
-    auto load = [&](f32x4& x) {
-        const float* row = row_ptr(qb, pb, stat_row(wave + kWaves * lr, N), N, V) + s0;
-        const int e = lj * kSpan;  // first element of the span within the slice
+    auto take = [&]() -> int {
+        int v = 0;
+        if (lane == 0) v = __hip_atomic_fetch_add(rowctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    static_assert(2 * TV_MAX_NODES <= 128 && kMaxSpans < 4096, "tag fields");
+    // load cursor: row li (claim index), span lj; past the last row the cursor
+    // stays on its last span and marks the loads as fillers
+    int li = take();
+    int lj = 0;
+    bool lvalid = li < nrows;
+    const float* lrow = row_ptr(qb, pb, stat_row(lvalid ? li : 0, N), N, V) + s0;
+    auto load = [&](f32x4& x, int& xt) {
+        const int e = lj * kSpan;
         if constexpr (VEC4) {
             const int v = e + 4 * lane;
-            const f32x4 t = *reinterpret_cast<const f32x4*>(row + min(v, nsl - 4));
+            const f32x4 t = *reinterpret_cast<const f32x4*>(lrow + min(v, nsl - 4));
 #pragma unroll
             for (int k = 0; k < 4; ++k) x[k] = v < nsl ? t[k] : -INFINITY;
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int v = e + lane + kWave * k;
-                const float t = row[min(v, nsl - 1)];
+                const float t = lrow[min(v, nsl - 1)];
                 x[k] = v < nsl ? t : -INFINITY;
             }
         }
-        const bool at_end = lr == last_lr && lj == last_lj;
-        lj = at_end ? lj : (lj == last_lj ? 0 : lj + 1);
-        lr = at_end ? lr : (lj == 0 ? lr + 1 : lr);
+        xt = lvalid ? (li << 12 | lj | (lj == nspan - 1 ? (int)0x80000000 : 0)) : -1;
+        if (!lvalid) return;
+        if (++lj == nspan) {
+            const int nxt = take();
+            if (nxt < nrows) {
+                li = nxt;
+                lj = 0;
+                lrow = row_ptr(qb, pb, stat_row(li, N), N, V) + s0;
+            } else {
+                lvalid = false;
+                lj = nspan - 1;
+            }
+        }
     };
 
     float m = -INFINITY, bv = -INFINITY;
     double s = 0.0;
     int bi = 0x7fffffff;
-    auto process = [&](const f32x4& x) {
-        if (pj == 0) {
+    bool done = false;
+    auto process = [&](const f32x4& x, int tag) {
+        if (tag == -1) {
+            done = true;
+            return;
+        }
+        const int j = tag & 4095;
+        if (j == 0) {
             m = -INFINITY;
             s = 0.0;
             bv = -INFINITY;
             bi = 0x7fffffff;
         }
-        const int e = pj * kSpan;
+        const int e = j * kSpan;
         if constexpr (GREEDY) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -282,8 +315,8 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
                 s += (double)(e0 + e1);
             }
         }
-        if (pj == nspan - 1) {  // the row is done: reduce over the wave and publish
-            const int r = stat_row(wave + kWaves * pr, N);
+        if (tag < 0) {  // the row's last span: reduce over the wave and publish
+            const int r = stat_row((tag >> 12) & 127, N);
             if constexpr (GREEDY) {
                 group_argmax_dpp(bv, bi, kWave);
                 if (lane == 0) st_dev(&stats[(size_t)r * W + w], pack2(bv, __int_as_float(bi)));
@@ -294,26 +327,25 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
                 if (lane == 0) st_dev(&stats[(size_t)r * W + w], pack2(M, (float)S));
             }
         }
-        if (++pj == nspan) {
-            pj = 0;
-            ++pr;
-        }
     };
 
-    f32x4 xa[kGroup], xb[kGroup];
+    // the scalar-load path holds half the groups (it stays within 128 VGPRs)
+    constexpr int NG = VEC4 ? kGroup : kGroup / 2;
+    f32x4 xa[NG], xb[NG];
+    int ta[NG], tb[NG];
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) load(xa[i]);
-    while (pr < myrows) {
+    for (int i = 0; i < NG; ++i) load(xa[i], ta[i]);
+    while (!done) {
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) load(xb[i]);
+        for (int i = 0; i < NG; ++i) load(xb[i], tb[i]);
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i)
-            if (pr < myrows) process(xa[i]);
+        for (int i = 0; i < NG; ++i)
+            if (!done) process(xa[i], ta[i]);
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) load(xa[i]);
+        for (int i = 0; i < NG; ++i) load(xa[i], ta[i]);
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i)
-            if (pr < myrows) process(xb[i]);
+        for (int i = 0; i < NG; ++i)
+            if (!done) process(xb[i], tb[i]);
     }
 }
 
@@ -536,7 +568,7 @@ __device__ __forceinline__ int slice_draw(const float* res, int nsl, double tau,
 
 // ---------------------------------------------------------------- the kernel --
 template <bool GREEDY, bool VEC4>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void spec_accept_kernel(const AccArgs a) {
+__global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) {
     const int tid = threadIdx.x;
     const int team = blockIdx.x / a.W;
     const int w = blockIdx.x % a.W;
@@ -556,21 +588,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     __shared__ double s_tab[32];
     __shared__ double s_rejZ[GREEDY ? 1 : TV_MAX_NODES];
     __shared__ int s_rej[GREEDY ? 1 : TV_MAX_NODES];
-    __shared__ float s_wx[2];
+    __shared__ float s_wx[2], s_nwx[2];
     __shared__ double s_oexcl;
-    __shared__ int s_ok, s_last, s_tok, s_owner, s_fallback, s_hitw[kWaves], s_lastw[kWaves];
+    __shared__ int s_ok, s_tok, s_owner, s_fallback, s_rowctr, s_hitw[kWaves], s_lastw[kWaves];
     __shared__ uint64_t s_base;
 
     if (tid < 32) exp2_table(s_tab, tid);
     TeamSync sync;
-    sync.line = GREEDY ? nullptr : a.ctrl + (size_t)team * kCtrlLine;
-    sync.arrive = GREEDY ? nullptr : a.arrive + (size_t)team * kMaxTeamSize;
+    sync.line = a.ctrl + (size_t)team * kCtrlLine;
+    sync.arrive = a.arrive + (size_t)team * kMaxTeamSize;
     sync.k = 0;
     sync.base = 0;
-    uint64_t gen = 0;
-    if constexpr (!GREEDY) {
-        if (tid == 0) gen = ld_dev(&sync.line[0]);  // used at the first barrier; the load overlaps the stream
-    }
+    // this call's tags start above the team's last generation (read before
+    // this member's first arrival; the load overlaps the first tree load)
+    if (tid == 0) s_base = (ld_dev(&sync.line[0]) + 1) << kTagShift;
     bool have_base = false;
 
     int iter = 0;
@@ -587,7 +618,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
                 ok = tid == 0 ? pr == -1 : (pr >= 0 && pr < tid);
             }
             const bool all_ok = __all(ok);
-            if (tid == 0) s_ok = all_ok;
+            if (tid == 0) {
+                s_ok = all_ok;
+                s_rowctr = 0;  // the previous sequence's stream ended before its team barrier
+            }
         }
         __syncthreads();
         int32_t* out_nodes = a.accepted + (size_t)b * N;
@@ -618,22 +652,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
             gp = pb[(size_t)gc * V + x];
         }
 
-        // ---- 1. slice statistics of every row ----
-        uint64_t* stats = GREEDY ? a.stats + (size_t)b * N * W
-                                 : a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)2 * N * W;
-        stream_slices<GREEDY, VEC4>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w);
+        // ---- 1. slice statistics of every row (double-buffered per team: a
+        // member may start the next sequence while member 0 still reads) ----
+        uint64_t* stats = a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)(GREEDY ? N : 2 * N) * W;
+        stream_slices<GREEDY, VEC4>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr);
+        // ---- 2. team barrier: every member's statistics are published ----
+        if (!have_base) {
+            sync.base = s_base;  // written before the tree barrier
+            have_base = true;
+        }
+        team_sync(sync, w, W);
         if constexpr (GREEDY) {
-            // ---- 2. the last member to publish merges and writes the path ----
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (tid == 0) {
-                const uint32_t prev =
-                    __hip_atomic_fetch_add(&a.counter[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                s_last = prev == (uint32_t)W - 1;
-                if (s_last) __hip_atomic_store(&a.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __syncthreads();
-            if (!s_last) continue;
+            // ---- member 0 merges and writes the path ----
+            if (w != 0) continue;
             int* s_amax = s_path;  // reuse: argmax per target row
             merge_greedy(stats, N, W, s_amax);
             for (int i = tid; i < N; i += kThreads) {
@@ -664,14 +695,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
             }
             __syncthreads();
         } else {
-            // ---- 3. barrier, then every member merges every row ----
-            if (!have_base) {
-                if (tid == 0) s_base = (gen + 1) << kTagShift;
-                __syncthreads();
-                sync.base = s_base;
-                have_base = true;
-            }
-            team_sync(sync, w, W);
+            // ---- 3. every member merges every row ----
             if (gc < N) {
                 s_gq[gc] = gq;
                 s_gp[gc] = gp;
@@ -725,22 +749,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
                                                         invSq, s_M[N + cc], (float)(1.0 / s_S[N + cc]), invZ, c,
                                                         nsl, s_res, x2l, &s_wx[1], &s_wx[0]);
                 const double smass = block_sum_d(part, s_wt);  // its barriers publish s_wx
-                double* slot = massb + (size_t)pass * W * kMassRec;
+                // publish and gather in one step: every word carries the step's tag,
+                // so a member polls the other members' words directly
+                uint64_t* slot = reinterpret_cast<uint64_t*>(massb + (size_t)pass * W * kMassRec);
+                const uint64_t tg = (uint64_t)exchange_tag(sync) << 32;
                 if (tid == 0) {
-                    st_dev_d(&slot[w * kMassRec + 0], smass);
-                    st_dev_d(&slot[w * kMassRec + 1], (double)s_wx[0]);  // new residual at the next token
-                    st_dev_d(&slot[w * kMassRec + 2], (double)s_wx[1]);  // stored residual before the pass
+                    const uint64_t mb = (uint64_t)__double_as_longlong(smass);
+                    st_dev(&slot[w * kMassRec + 0], tg | (uint32_t)mb);
+                    st_dev(&slot[w * kMassRec + 1], tg | (uint32_t)(mb >> 32));
+                    st_dev(&slot[w * kMassRec + 2], tg | __float_as_uint(s_wx[0]));  // new residual at the next token
+                    st_dev(&slot[w * kMassRec + 3], tg | __float_as_uint(s_wx[1]));  // stored residual before the pass
                 }
-                team_sync(sync, w, W);
-                // every member gathers the slice masses and the next sibling's residual
-                const double mt = tid < W ? ld_dev_d(&slot[tid * kMassRec + 0]) : 0.0;
                 const int xo = nxt < N ? s_draft[nxt] / a.slice : -1;
-                if (tid == xo) {
-                    s_wx[0] = (float)ld_dev_d(&slot[tid * kMassRec + 1]);
-                    s_wx[1] = (float)ld_dev_d(&slot[tid * kMassRec + 2]);
+                double mt = 0.0;
+                if (tid < W) {
+                    uint64_t e[kMassRec];
+                    gather_tagged(sync, &slot[tid * kMassRec], tg, e);
+                    mt = __longlong_as_double((long long)((e[1] << 32) | (uint32_t)e[0]));
+                    if (tid == xo) {
+                        s_nwx[0] = __uint_as_float((uint32_t)e[2]);
+                        s_nwx[1] = __uint_as_float((uint32_t)e[3]);
+                    }
                 }
                 double mexcl, Znew;
-                block_scan_d(mt, s_wt, mexcl, Znew);  // its barriers publish s_wx too
+                block_scan_d(mt, s_wt, mexcl, Znew);  // its barriers publish s_nwx
+                if (tid == 0) {
+                    s_wx[0] = s_nwx[0];
+                    s_wx[1] = s_nwx[1];
+                }
+                __syncthreads();
                 ++pass;
                 if (Znew > 0.0) {
                     if (tid < W) s_mass[tid] = mt;
@@ -878,7 +915,6 @@ int resident_capacity() {
                     return 0;
                 per_min = per < per_min ? per : per_min;
             }
-        if (per_min > 4) per_min = 4;  // a few members per CU cover HBM latency
         if (per_min < 1) return 0;
         cache[dev] = ncu * per_min;
     }
@@ -892,7 +928,7 @@ int make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
     int wmax = (V + kMinSlice - 1) / kMinSlice;
     if (wmax > kMaxTeamSize) wmax = kMaxTeamSize;
     // sampling keeps a member's residual slice in LDS
-    const int wmin = greedy ? 1 : (V + kMaxSlice - 1) / kMaxSlice;
+    const int wmin = greedy ? (V + kMaxSpans * kSpan - 1) / (kMaxSpans * kSpan) : (V + kMaxSlice - 1) / kMaxSlice;
     if (wmin > kMaxTeamSize) return TV_ERR_UNSUPPORTED;
     if (wmax < wmin) wmax = wmin;
     int W = cap / (B > 0 ? B : 1);
@@ -910,16 +946,16 @@ int make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
     pl.W = W;
     pl.nteams = nteams;
     pl.slice = slice;
+    // The control words (team lines, arrival words) sit at the same offsets
+    // for every shape and mode and stay valid for any later call (generation
+    // tags), so a workspace serves later calls of any shape without clearing.
     size_t off = 0;
     pl.ctrl_off = off;
-    if (!greedy) off += round_up((size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t), 256);
+    off += round_up((size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t), 256);
     pl.arrive_off = off;
-    if (!greedy) off += round_up((size_t)kMaxTeams * kMaxTeamSize * sizeof(uint64_t), 256);
-    pl.counter_off = off;
-    if (greedy) off += round_up((size_t)B * sizeof(uint32_t), 256);
+    off += round_up((size_t)kMaxTeams * kMaxTeamSize * sizeof(uint64_t), 256);
     pl.stats_off = off;
-    off += greedy ? round_up((size_t)B * N * W * sizeof(uint64_t), 256)
-                  : round_up((size_t)nteams * 2 * 2 * N * W * sizeof(uint64_t), 256);
+    off += round_up((size_t)nteams * 2 * (greedy ? N : 2 * N) * W * sizeof(uint64_t), 256);
     pl.mass_off = off;
     if (!greedy) off += round_up((size_t)nteams * N * W * kMassRec * sizeof(double), 256);
     pl.total = off;
@@ -964,9 +1000,8 @@ extern "C" int tv_spec_accept(const float* q_logits, const float* p_logits, cons
     a.accept_len = accept_len;
     a.accepted = accepted_nodes;
     a.tokens = out_tokens;
-    a.ctrl = greedy ? nullptr : reinterpret_cast<uint64_t*>(ws + pl.ctrl_off);
-    a.arrive = greedy ? nullptr : reinterpret_cast<uint64_t*>(ws + pl.arrive_off);
-    a.counter = greedy ? reinterpret_cast<uint32_t*>(ws + pl.counter_off) : nullptr;
+    a.ctrl = reinterpret_cast<uint64_t*>(ws + pl.ctrl_off);
+    a.arrive = reinterpret_cast<uint64_t*>(ws + pl.arrive_off);
     a.stats = reinterpret_cast<uint64_t*>(ws + pl.stats_off);
     a.mass = greedy ? nullptr : reinterpret_cast<double*>(ws + pl.mass_off);
     a.B = B;
