@@ -17,16 +17,15 @@
 //     exp((x - max)/T) -- or the max and its first index in greedy mode.
 //     The logits the walk tests, q_parent(c)(x_c) and p_c(x_c), are gathered
 //     while the stream is in flight.
-//  2. A team barrier; greedy: member 0 merges the argmax of every target row
-//     and writes the path.
+//  2. Greedy: every member merges the argmax of every target row from the
+//     other members' entries; member 0 writes the path.
 //  3. Sampling: every member merges the statistics of
 //     every row and runs the same walk redundantly: decisions need only the
 //     merged statistics and the gathered logits, so all members agree bit for
 //     bit without communicating.
 //  4. A rejection costs one pass over the slices: the residual
-//     max(0, R - P_c) replaces the member's slice of R in LDS, its slice mass
-//     and the residual at the next sibling's token are published, and a team
-//     barrier follows.
+//     max(0, R - P_c) replaces the member's slice of R in LDS, and its slice
+//     mass and the residual at the next sibling's token are exchanged.
 //  5. The extra token: every member knows every slice's mass (from the last
 //     residual pass, or from the statistics when drawing from a target row),
 //     so the member whose slice holds U * total scans its slice alone.
@@ -36,14 +35,14 @@
 // the gathered logits.  Decisions can differ from exact arithmetic only within
 // ~1e-6 of a boundary.
 //
-// Team barrier: every member stores a generation-tagged arrival word and polls
-// the words of all the others (no relay through one member).  Data crossing
-// members goes through device-scope loads and stores (coherent across XCDs
-// without L2 write-back or invalidation); a member waits for its own stores
-// to land before it arrives.  Tags grow monotonically per team across calls
-// (member 0 advances the team's generation word once the first barrier of a
-// call has gathered everyone), so the control words never need clearing
-// after the workspace was zero-filled once.
+// Cross-member data (statistics entries, walk-step records) are 64-bit words
+// carrying a tag (call generation, sequence or step) in their upper half,
+// written with device-scope stores (coherent across XCDs without L2
+// write-back or invalidation); a reader polls the words it needs until they
+// carry the expected tag, so no barrier separates writer and reader.  Member
+// 0 advances the team's generation word once its first merge of a call has
+// seen every member's entries (every member read the word before streaming),
+// so nothing in the workspace needs clearing after it was zero-filled once.
 // The grid never exceeds the device's resident capacity, so all members of a
 // team run together; spins are bounded.
 #include <float.h>
@@ -66,14 +65,14 @@ constexpr int kMaxSpans = 4095;      // greedy: spans of 256 logits per slice, a
 constexpr int kSpan = 4 * kWave;     // logits one wave covers with one 16-byte load per lane
 constexpr int kGroup = 4;            // spans per prefetch group (two groups in flight per wave)
 constexpr int kCtrlLine = 16;        // u64 words per team: [0] generation, [2] time-out flag
-constexpr int kTagShift = 24;        // barrier tag = (generation << 24) + barrier index
+constexpr int kTagShift = 24;        // TeamSync::base = generation << kTagShift
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int kMassRec = 4;          // tagged u64 words per (pass, member): mass (two halves), new and old
                                      // residual at the next token
 
 struct AcceptPlan {
     int W, nteams, slice;
-    size_t ctrl_off, arrive_off, stats_off, mass_off, total;
+    size_t ctrl_off, stats_off, mass_off, total;
 };
 
 struct AccArgs {
@@ -85,8 +84,7 @@ struct AccArgs {
     int32_t* accepted;
     int32_t* tokens;
     uint64_t* ctrl;      // [kMaxTeams][kCtrlLine]
-    uint64_t* arrive;    // [kMaxTeams][kMaxTeamSize]
-    uint64_t* stats;     // [nteams][2][2N][W] (max, sum); greedy [nteams][2][N][W] (max, index)
+    uint64_t* stats;     // [nteams][2][2N][W][2] tagged (max), (sum); greedy [nteams][2][N][W][2] (max), (index)
     double* mass;        // sampling: [nteams][N][W][kMassRec]
     int B, N, V, W, slice, nteams;
     float c;             // log2(e) / T
@@ -101,58 +99,31 @@ __device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
 __device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
     return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t pack2(float a, float b) {
-    return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-}
 __device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
-__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
 struct TeamSync {
     uint64_t* line;    // this team's control line
-    uint64_t* arrive;  // this team's arrival words
     uint64_t base;     // (generation of this call) << kTagShift
-    uint32_t k;        // barriers passed so far in this call
+    uint32_t k;        // walk exchanges so far in this call
 };
 
-__device__ __forceinline__ void team_sync(TeamSync& s, int w, int W) {
-    ++s.k;
-    const uint64_t tag = s.base + s.k;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's device-scope stores have landed
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (t == 0) st_dev(&s.arrive[w], tag);
-    if (t < W && t != w) {  // every member watches every other member's word
-        uint32_t spins = 0;
-        while (ld_dev(&s.arrive[t]) < tag) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins > kSpinLimit) {
-                st_dev(&s.line[2], 1ull);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-    // every member has read the generation word by now (before its first
-    // arrival): the next call starts after this generation
-    if (s.k == 1 && w == 0 && t == 0) st_dev(&s.line[0], s.base >> kTagShift);
-}
-
-// Walk steps exchange tagged words instead of passing a barrier: the tag is
-// (generation << 12 | step) in the upper 32 bits of every 64-bit word, so a
-// word from an earlier step, or from an earlier call, is told apart (a slot
-// would have to go unused for 2^20 calls and then be reused at the same step
-// to be mistaken).  Steps count on with the team's barrier index.
+// Walk steps exchange tagged words: the tag is (generation << 12 | step) in
+// the upper 32 bits of every 64-bit word, so a word from an earlier step, or
+// from an earlier call, is told apart (a slot would have to go unused for 2^20
+// calls and then be reused at the same step to be mistaken).  Statistics
+// entries use (generation << 12 | sequence of the team) the same way.
 __device__ __forceinline__ uint32_t exchange_tag(TeamSync& s) {
     ++s.k;
     return (uint32_t)(((s.base >> kTagShift) << 12) | (s.k & 0xfffu));
 }
-// Poll one member's kMassRec words until all carry tag `tg` (upper half).
-__device__ __forceinline__ void gather_tagged(TeamSync& s, const uint64_t* src, uint64_t tg, uint64_t* e) {
+// Poll one member's first nw words until all carry tag `tg` (upper half).
+__device__ __forceinline__ void gather_tagged(TeamSync& s, const uint64_t* src, uint64_t tg, int nw, uint64_t* e) {
     uint32_t spins = 0;
     for (;;) {
         bool ok = true;
 #pragma unroll
         for (int i = 0; i < kMassRec; ++i) {
+            if (i >= nw) continue;
             e[i] = ld_dev(&src[i]);
             ok = ok && (e[i] & 0xffffffff00000000ull) == tg;
         }
@@ -163,6 +134,14 @@ __device__ __forceinline__ void gather_tagged(TeamSync& s, const uint64_t* src, 
             return;
         }
     }
+}
+
+// After the first merge of a call every member of the team has read the
+// team's generation word (before it streamed): member 0 advances it for the
+// next call.
+__device__ __forceinline__ void advance_generation(TeamSync& s, int w, bool& done) {
+    if (!done && w == 0 && threadIdx.x == 0) st_dev(&s.line[0], s.base >> kTagShift);
+    done = true;
 }
 
 // ------------------------------------------------------------------ helpers --
@@ -232,7 +211,8 @@ __device__ __forceinline__ const float* row_ptr(const float* qb, const float* pb
 // stored as fp32), greedy (max, first index).
 template <bool GREEDY, bool VEC4>
 __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, int nrows, int N, int V, int s0,
-                                              int nsl, float c, uint64_t* stats, int W, int w, int* rowctr) {
+                                              int nsl, float c, uint64_t* stats, int W, int w, int* rowctr,
+                                              uint64_t tg) {
     const int lane = threadIdx.x & 63;
     const int nspan = (nsl + kSpan - 1) / kSpan;
     auto take = [&]() -> int {
@@ -319,12 +299,18 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
             const int r = stat_row((tag >> 12) & 127, N);
             if constexpr (GREEDY) {
                 group_argmax_dpp(bv, bi, kWave);
-                if (lane == 0) st_dev(&stats[(size_t)r * W + w], pack2(bv, __int_as_float(bi)));
+                if (lane == 0) {
+                    st_dev(&stats[2 * ((size_t)r * W + w)], tg | __float_as_uint(bv));
+                    st_dev(&stats[2 * ((size_t)r * W + w) + 1], tg | (uint32_t)bi);
+                }
             } else {
                 const float M = group_max_dpp(m, kWave);
                 const double f = (m == -INFINITY) ? 0.0 : (double)__builtin_amdgcn_exp2f((m - M) * c);
                 const double S = group_sum_dpp(s * f, kWave);
-                if (lane == 0) st_dev(&stats[(size_t)r * W + w], pack2(M, (float)S));
+                if (lane == 0) {
+                    st_dev(&stats[2 * ((size_t)r * W + w)], tg | __float_as_uint(M));
+                    st_dev(&stats[2 * ((size_t)r * W + w) + 1], tg | __float_as_uint((float)S));
+                }
             }
         }
     };
@@ -360,14 +346,46 @@ __device__ __forceinline__ int lanes_per_row(int W) {
 }
 
 
+// Statistics entries are two tagged words, (tag, first value) and (tag, second
+// value); a merge polls them until every word carries the sequence's tag, so
+// no team barrier separates the stream from the merge.  Lanes whose entries
+// are not yet published load them again.
+constexpr int kBatch = 1;
+
+template <int K>
+__device__ __forceinline__ void poll_entries(const uint64_t* stats, const uint32_t (&idx)[K][4], uint64_t tg,
+                                             uint64_t (&e)[K][4][2], uint64_t* line) {
+    auto fetch = [&]() {
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e[k][i][0] = ld_dev(&stats[2 * (size_t)idx[k][i]]);
+                e[k][i][1] = ld_dev(&stats[2 * (size_t)idx[k][i] + 1]);
+                ok = ok && (e[k][i][0] & 0xffffffff00000000ull) == tg && (e[k][i][1] & 0xffffffff00000000ull) == tg;
+            }
+        return ok;
+    };
+    bool ok = fetch();
+    uint32_t spins = 0;
+    while (__ballot(!ok)) {
+        __builtin_amdgcn_s_sleep(1);
+        if (!ok) ok = fetch();
+        if (++spins > kSpinLimit) {
+            if (!ok) st_dev(&line[2], 1ull);
+            break;
+        }
+    }
+}
+
 // Sampling: merged max sM[r] and normaliser sS[r] = sum_w s_w exp((m_w - M)/T)
-// of every streamed row, from stats[r][W].  Each wave issues the loads of
-// kBatch row groups before reducing any of them.  The factors are fp32
+// of every streamed row, from the entries [r][W].  Each wave issues the loads
+// of kBatch row groups before reducing any of them.  The factors are fp32
 // (relative error ~1e-7), the sums fp64.
-constexpr int kBatch = 4;
 
 __device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows, int N, int W, float c, float* sM,
-                                               double* sS) {
+                                               double* sS, uint64_t tg, uint64_t* line) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lpr = lanes_per_row(W);
@@ -376,26 +394,28 @@ __device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows,
     const int g = lane / lpr, li = lane % lpr;
     for (int r0 = wave * rpw * kBatch; r0 < nrows; r0 += kWaves * rpw * kBatch) {
         // loads are unconditional (indices clamped) so that they all stay in flight
-        uint64_t e[kBatch][4];
+        uint32_t idx[kBatch][4];  // entry index r W + member (< 2^15)
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int ri = r0 + k * rpw + g;
             const int r = stat_row(min(ri, nrows - 1), N);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) e[k][i] = ld_dev(&stats[(size_t)r * W + min(li + lpr * i, W - 1)]);
+            for (int i = 0; i < 4; ++i) idx[k][i] = (uint32_t)(r * W + min(li + lpr * i, W - 1));
         }
+        uint64_t e[kBatch][4][2];
+        poll_entries<kBatch>(stats, idx, tg, e, line);
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int ri = r0 + k * rpw + g;
             float mk[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mk[i] = (i < per && li + lpr * i < W) ? lo_f(e[k][i]) : -INFINITY;
+            for (int i = 0; i < 4; ++i) mk[i] = (i < per && li + lpr * i < W) ? lo_f(e[k][i][0]) : -INFINITY;
             float M = fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3]));
             M = group_max_dpp(M, lpr);
             double S = 0.0;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (mk[i] != -INFINITY) S += (double)hi_f(e[k][i]) * (double)__builtin_amdgcn_exp2f((mk[i] - M) * c);
+                if (mk[i] != -INFINITY) S += (double)lo_f(e[k][i][1]) * (double)__builtin_amdgcn_exp2f((mk[i] - M) * c);
             S = group_sum_dpp(S, lpr);
             if (ri < nrows && li == 0) {
                 const int r = stat_row(ri, N);
@@ -406,8 +426,9 @@ __device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows,
     }
 }
 
-// Greedy: argmax of every target row 0..N-1 from stats[r][W].
-__device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W, int* amax) {
+// Greedy: argmax of every target row 0..N-1 from the entries [r][W].
+__device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W, int* amax, uint64_t tg,
+                                             uint64_t* line) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lpr = lanes_per_row(W);
@@ -415,13 +436,15 @@ __device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W
     const int per = (W + lpr - 1) / lpr;
     const int g = lane / lpr, li = lane % lpr;
     for (int r0 = wave * rpw * kBatch; r0 < N; r0 += kWaves * rpw * kBatch) {
-        uint64_t e[kBatch][4];
+        uint32_t idx[kBatch][4];  // entry index r W + member (< 2^15)
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int r = min(r0 + k * rpw + g, N - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) e[k][i] = ld_dev(&stats[(size_t)r * W + min(li + lpr * i, W - 1)]);
+            for (int i = 0; i < 4; ++i) idx[k][i] = (uint32_t)(r * W + min(li + lpr * i, W - 1));
         }
+        uint64_t e[kBatch][4][2];
+        poll_entries<kBatch>(stats, idx, tg, e, line);
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int r = r0 + k * rpw + g;
@@ -429,7 +452,7 @@ __device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W
             int bi = 0x7fffffff;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (i < per && li + lpr * i < W) argmax_merge(bv, bi, lo_f(e[k][i]), __float_as_int(hi_f(e[k][i])));
+                if (i < per && li + lpr * i < W) argmax_merge(bv, bi, lo_f(e[k][i][0]), (int)(uint32_t)e[k][i][1]);
             group_argmax_dpp(bv, bi, lpr);
             if (r < N && li == 0) amax[r] = bi;
         }
@@ -596,13 +619,12 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
     if (tid < 32) exp2_table(s_tab, tid);
     TeamSync sync;
     sync.line = a.ctrl + (size_t)team * kCtrlLine;
-    sync.arrive = a.arrive + (size_t)team * kMaxTeamSize;
     sync.k = 0;
     sync.base = 0;
     // this call's tags start above the team's last generation (read before
     // this member's first arrival; the load overlaps the first tree load)
     if (tid == 0) s_base = (ld_dev(&sync.line[0]) + 1) << kTagShift;
-    bool have_base = false;
+    bool have_base = false, gen_done = false;
 
     int iter = 0;
     for (int b = team; b < a.B; b += a.nteams, ++iter) {
@@ -620,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             const bool all_ok = __all(ok);
             if (tid == 0) {
                 s_ok = all_ok;
-                s_rowctr = 0;  // the previous sequence's stream ended before its team barrier
+                s_rowctr = 0;  // every wave finished the previous stream (workgroup barriers followed it)
             }
         }
         __syncthreads();
@@ -652,21 +674,28 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             gp = pb[(size_t)gc * V + x];
         }
 
-        // ---- 1. slice statistics of every row (double-buffered per team: a
-        // member may start the next sequence while member 0 still reads) ----
-        uint64_t* stats = a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)(GREEDY ? N : 2 * N) * W;
-        stream_slices<GREEDY, VEC4>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr);
-        // ---- 2. team barrier: every member's statistics are published ----
+        // ---- 1. slice statistics of every row, published as entries tagged
+        // with (call generation, sequence of this team).  Double-buffered per
+        // team: a member starts streaming sequence i + 1 only after it merged
+        // sequence i, which needs every member's entries of i, so no member can
+        // overwrite a buffer that another still merges ----
         if (!have_base) {
-            sync.base = s_base;  // written before the tree barrier
+            // written before the tree barrier; uniform (kept in scalar registers)
+            sync.base = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_base >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)s_base);
             have_base = true;
         }
-        team_sync(sync, w, W);
+        const uint64_t stag = (uint64_t)(uint32_t)(((sync.base >> kTagShift) << 12) | ((uint32_t)iter & 0xfffu)) << 32;
+        uint64_t* stats = a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)2 * (GREEDY ? N : 2 * N) * W;
+        stream_slices<GREEDY, VEC4>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag);
         if constexpr (GREEDY) {
-            // ---- member 0 merges and writes the path ----
-            if (w != 0) continue;
+            // ---- 2. every member merges (seeing every member's entries), member 0
+            // writes the path ----
             int* s_amax = s_path;  // reuse: argmax per target row
-            merge_greedy(stats, N, W, s_amax);
+            merge_greedy(stats, N, W, s_amax, stag, sync.line);
+            __syncthreads();
+            advance_generation(sync, w, gen_done);
+            if (w != 0) continue;
             for (int i = tid; i < N; i += kThreads) {
                 out_nodes[i] = -1;
                 out_toks[i] = -1;
@@ -700,8 +729,9 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 s_gq[gc] = gq;
                 s_gp[gc] = gp;
             }
-            merge_sampling(stats, nrows, N, W, c, s_M, s_S);
+            merge_sampling(stats, nrows, N, W, c, s_M, s_S, stag, sync.line);
             __syncthreads();
+            advance_generation(sync, w, gen_done);
 
             // ---- the walk (identical on every member) ----
             const double inv_t64 = a.inv_t64;
@@ -763,8 +793,9 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 const int xo = nxt < N ? s_draft[nxt] / a.slice : -1;
                 double mt = 0.0;
                 if (tid < W) {
-                    uint64_t e[kMassRec];
-                    gather_tagged(sync, &slot[tid * kMassRec], tg, e);
+                    // the residuals at the next token only from the member that owns it
+                    uint64_t e[kMassRec] = {0, 0, 0, 0};
+                    gather_tagged(sync, &slot[tid * kMassRec], tg, tid == xo ? kMassRec : 2, e);
                     mt = __longlong_as_double((long long)((e[1] << 32) | (uint32_t)e[0]));
                     if (tid == xo) {
                         s_nwx[0] = __uint_as_float((uint32_t)e[2]);
@@ -815,9 +846,9 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 if (res_active) {
                     mt = s_mass[tid];
                 } else {
-                    const uint64_t e = ld_dev(&stats[(size_t)u * W + tid]);
-                    mt = lo_f(e) == -INFINITY ? 0.0
-                                              : (double)hi_f(e) * (double)__builtin_amdgcn_exp2f((lo_f(e) - s_M[u]) * c);
+                    const float em = lo_f(ld_dev(&stats[2 * ((size_t)u * W + tid)]));
+                    const float es = lo_f(ld_dev(&stats[2 * ((size_t)u * W + tid) + 1]));
+                    mt = em == -INFINITY ? 0.0 : (double)es * (double)__builtin_amdgcn_exp2f((em - s_M[u]) * c);
                 }
             }
             double mexcl, total;
@@ -946,16 +977,14 @@ int make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
     pl.W = W;
     pl.nteams = nteams;
     pl.slice = slice;
-    // The control words (team lines, arrival words) sit at the same offsets
-    // for every shape and mode and stay valid for any later call (generation
-    // tags), so a workspace serves later calls of any shape without clearing.
+    // The team lines sit at the same offsets for every shape and mode and
+    // every other word is tagged with its call's generation, so a workspace
+    // serves later calls of any shape without clearing.
     size_t off = 0;
     pl.ctrl_off = off;
     off += round_up((size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t), 256);
-    pl.arrive_off = off;
-    off += round_up((size_t)kMaxTeams * kMaxTeamSize * sizeof(uint64_t), 256);
     pl.stats_off = off;
-    off += round_up((size_t)nteams * 2 * (greedy ? N : 2 * N) * W * sizeof(uint64_t), 256);
+    off += round_up((size_t)nteams * 2 * 2 * (greedy ? N : 2 * N) * W * sizeof(uint64_t), 256);
     pl.mass_off = off;
     if (!greedy) off += round_up((size_t)nteams * N * W * kMassRec * sizeof(double), 256);
     pl.total = off;
@@ -1001,7 +1030,6 @@ extern "C" int tv_spec_accept(const float* q_logits, const float* p_logits, cons
     a.accepted = accepted_nodes;
     a.tokens = out_tokens;
     a.ctrl = reinterpret_cast<uint64_t*>(ws + pl.ctrl_off);
-    a.arrive = reinterpret_cast<uint64_t*>(ws + pl.arrive_off);
     a.stats = reinterpret_cast<uint64_t*>(ws + pl.stats_off);
     a.mass = greedy ? nullptr : reinterpret_cast<double*>(ws + pl.mass_off);
     a.B = B;
@@ -1016,7 +1044,8 @@ extern "C" int tv_spec_accept(const float* q_logits, const float* p_logits, cons
     const bool vec4 = (V % 4 == 0) && aligned(q_logits, 16) && (greedy || aligned(p_logits, 16));
     // The grid never exceeds the resident capacity from the occupancy query, so
     // once earlier work on the stream drains every member is resident and the
-    // team barriers make progress (their spins are bounded regardless).
+    // polls for other members' words make progress (their spins are bounded
+    // regardless).
     hipLaunchKernelGGL(pick(greedy, vec4), dim3(pl.nteams * pl.W), dim3(kThreads), 0, (hipStream_t)stream, a);
     return launch_status();
 }
