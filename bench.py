@@ -167,6 +167,21 @@ def time_calls(fns, steps, stream, torch, lead_cycles):
     return total, per
 
 
+def time_batch(fn, steps, stream, torch, lead_cycles):
+    """Mean device time per call of ``steps`` back-to-back launches of one call
+    (queued behind a spin kernel, so host launch latency is hidden)."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(lead_cycles))
+    start.record(stream)
+    for s in range(steps):
+        fn(s)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def copy_calibration(torch, dev, nbytes=COPY_CAL_BYTES):
     """One plain elementwise copy (read nbytes, write nbytes) outside the timed
     region: under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the factor
@@ -298,13 +313,15 @@ def main():
     ms_step = total_ms / args.steps
     total_g, _ = time_calls({"step": full("greedy")}, args.steps, stream, torch, lead(args.steps))
     ms_greedy = total_g / args.steps
-    # per-call durations inside the step (events on the launch stream, device time only)
-    _, per = time_calls({"mask": lambda s: copies[s % ncopies]["sample"].mask(),
-                         "attention": lambda s: copies[s % ncopies]["sample"].attention(),
-                         "accept": lambda s: copies[s % ncopies]["sample"].accept()}, args.steps, stream, torch,
-                        lead(3 * args.steps))
-    _, per_g = time_calls({"accept_greedy": lambda s: copies[s % ncopies]["greedy"].accept()}, args.steps, stream,
-                          torch, lead(args.steps))
+    # per-call durations: `steps` launches of one call back to back (rotating
+    # over the input copies) between two events on the launch stream
+    calls = {"mask": lambda s: copies[s % ncopies]["sample"].mask(),
+             "attention": lambda s: copies[s % ncopies]["sample"].attention(),
+             "accept": lambda s: copies[s % ncopies]["sample"].accept(),
+             "accept_greedy": lambda s: copies[s % ncopies]["greedy"].accept()}
+    per_all = {n: time_batch(fn, args.steps, stream, torch, lead(args.steps)) for n, fn in calls.items()}
+    per = {k: per_all[k] for k in ("mask", "attention", "accept")}
+    per_g = {"accept_greedy": per_all["accept_greedy"]}
 
     nodes = w.B * (w.N - 1)
     value = nodes / (ms_step / 1e3)
