@@ -983,11 +983,15 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         interleave_qk_exp();
         load_tile(t + 3, ld);
         // step 2
+        // (the P.V steps run at raised wave priority: the SIMD's other wave is
+        // then in its exponentials, which fill the MFMA gaps)
+        __builtin_amdgcn_s_setprio(1);
         read_v(va, 0, 0, vl[0], vh[0]);
         read_v(va, 0, 1, vl[1], vh[1]);
         store_tile(t + 2, st);
         pv(vl[0], vh[0], pf[0]);
         pv(vl[1], vh[1], pf[1]);
+        __builtin_amdgcn_s_setprio(0);
         // step 3
         __syncthreads();
         // step 4 (past the last tile the scores come from a stage no tile
@@ -999,10 +1003,12 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         softmax_exp(s_b, mc, pf);
         interleave_qk_exp();
         // step 5
+        __builtin_amdgcn_s_setprio(1);
         read_v(va, 1, 0, vl[0], vh[0]);
         read_v(va, 1, 1, vl[1], vh[1]);
         pv(vl[0], vh[0], pf[0]);
         pv(vl[1], vh[1], pf[1]);
+        __builtin_amdgcn_s_setprio(0);
         sb = sb_next;
     };
 
