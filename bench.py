@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--temperature", type=float, default=None, help="sampling temperature (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP-graph replays")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the step instead of back-to-back launches")
     return ap.parse_args()
 
 
@@ -139,32 +140,6 @@ def sleep_cycles_per_ms(torch, stream):
     b.record(stream)
     torch.cuda.synchronize()
     return cyc / max(a.elapsed_time(b), 1e-3)
-
-
-def time_calls(fns, steps, stream, torch, lead_cycles):
-    """Events around each named call of every step; returns total ms and per-call mean ms.
-
-    A spin kernel of ``lead_cycles`` runs first, so the host has queued every
-    call before the device reaches them: the event pairs then bracket device
-    time only, not host launch latency."""
-    names = list(fns)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(lead_cycles))
-    start.record(stream)
-    for s in range(steps):
-        e = evs[s]
-        e[0].record(stream)
-        for k, n in enumerate(names):
-            fns[n](s)
-            e[k + 1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total = start.elapsed_time(end)
-    per = {n: sum(evs[s][k].elapsed_time(evs[s][k + 1]) for s in range(steps)) / steps for k, n in enumerate(names)}
-    return total, per
 
 
 def time_batch(fn, steps, stream, torch, lead_cycles):
@@ -287,7 +262,7 @@ def main():
         copies[s % ncopies]["sample"].run()
         copies[s % ncopies]["greedy"].run()
     torch.cuda.synchronize()
-    use_graph = not args.eager
+    use_graph = args.graph
     if use_graph:
         for c in copies:
             c["sample"].capture(torch, stream)
@@ -309,10 +284,8 @@ def main():
     lead = lambda calls: cyc_ms * max(2.0, 0.05 * calls)
 
     # timed: whole steps, sampling mode (headline)
-    total_ms, _ = time_calls({"step": full("sample")}, args.steps, stream, torch, lead(args.steps))
-    ms_step = total_ms / args.steps
-    total_g, _ = time_calls({"step": full("greedy")}, args.steps, stream, torch, lead(args.steps))
-    ms_greedy = total_g / args.steps
+    ms_step = time_batch(full("sample"), args.steps, stream, torch, lead(3 * args.steps))
+    ms_greedy = time_batch(full("greedy"), args.steps, stream, torch, lead(3 * args.steps))
     # per-call durations: `steps` launches of one call back to back (rotating
     # over the input copies) between two events on the launch stream
     calls = {"mask": lambda s: copies[s % ncopies]["sample"].mask(),
@@ -369,7 +342,7 @@ def main():
         "config": {"workload": f"{w.name}: {CONFIG_TEXT[w.name]}", "batch": w.B, "tree_nodes": w.N,
                    "draft_nodes": w.N - 1, "heads_q_kv": [w.Hq, w.Hkv], "head_dim": w.D, "kv_len": w.L,
                    "vocab": w.V, "mode": f"sampling T={T}", "input_copies": ncopies,
-                   "launch": "hip-graph replay" if use_graph else "eager"},
+                   "launch": "hip-graph replay" if use_graph else "back-to-back launches on one stream"},
         "roofline": roof,
         "calls_us": {k: round(v * 1e3, 3) for k, v in {**per, **per_g}.items()},
         "attention": {"GB/s": round(attn_gbs, 1), "TFLOP/s": round(attn_tflops, 3),
