@@ -108,8 +108,8 @@ def test_attention_tiny_full_compare(tv, w):
     _attn_check(_np(out).astype(np.float64), ref, w.name)
 
 
-# shapes hitting each row packing (R = G*N <= 32, <= 64, > 64), ragged key tails,
-# single-key caches and splits
+# shapes hitting each row packing (R = G*N <= 32, <= 64, <= 128, > 128), ragged
+# key tails, single-key caches, empty caches, several row tiles and splits
 @pytest.mark.parametrize("B,N,Hq,Hkv,L,tree", [
     (1, 1, 1, 1, 1, "chain"),
     (2, 1, 8, 8, 0, "chain"),
@@ -121,6 +121,10 @@ def test_attention_tiny_full_compare(tv, w):
     (2, 7, 16, 1, 200, "random"),
     (1, 64, 8, 8, 1, "random"),
     (1, 40, 2, 2, 4097, "random"),
+    (1, 64, 4, 1, 0, "random"),
+    (2, 33, 8, 2, 700, "random"),
+    (1, 64, 16, 2, 3000, "random"),
+    (1, 17, 16, 1, 128, "chain"),
 ])
 def test_attention_shapes(tv, B, N, Hq, Hkv, L, tree):
     w = Workload("shape", B=B, N=N, Hq=Hq, Hkv=Hkv, D=128, L=L, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),

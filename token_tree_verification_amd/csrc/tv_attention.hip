@@ -192,6 +192,13 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
                  : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
                  : "memory", "m0");
 }
+// Same copy with a uniform 64-bit base and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // LDS accesses by byte address (32-bit, address space 3).
@@ -708,50 +715,52 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
     merge_splits<kThreads, ROWS>(a, lds, &s_last, grp, row0, nrows, b, g);
 }
 
-// Large row groups (R > 128): eight waves (two per SIMD) own 256 query rows
-// and step through 64-key tiles.  K/V tiles are staged through registers:
-// each wave loads its 4 KB share of a tile with coalesced 16-byte loads one
-// iteration ahead, converts the V half to fp16 in registers and writes both
-// halves into a four-stage LDS ring with swizzled chunks.  The loop is
-// software-pipelined so that the score MFMAs of the next 32-key block are in
-// flight while the vector ALUs run the softmax of the current block, with one
-// barrier per tile:
-//   step 1  S(t,1) = K(t,1) Q^T       ||  softmax of S(t,0) -> P(t,0);
-//           loads of tile t+3 issued
-//   step 2  O^T += V(t,0)^T P(t,0)^T  ||  tile t+2 (loaded in step 1 of the
-//           previous tile) converted and written to its stage
-//   step 3  barrier: tile t+2 visible to every wave
-//   step 4  S(t+1,0) = K(t+1,0) Q^T   ||  softmax of S(t,1) -> P(t,1)
-//   step 5  O^T += V(t,1)^T P(t,1)^T
-// Tile t+2 is written into the stage of tile t-2, whose last reads ended
-// before the previous barrier.  The softmax sums the fp16-rounded P it hands
-// to the MFMA (v_dot2 with fp32 accumulation), so the normaliser matches the
-// weights used.
+// fp16 packing for the large-row kernel below
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-template <bool B>
-struct Flag {
-    static constexpr bool value = B;
-};
-
 __device__ __forceinline__ uint32_t pack_f16(float x, float y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, f16x2));
 }
 
+// Large row groups (R > 128).  Eight waves (two per SIMD) own 256 query
+// rows, 32 each, and stream 64-key tiles of K and V through a five-stage LDS
+// ring.  Per 32-key block j every wave issues one stream in a fixed order:
+//   O^T  += V(j-1)^T P(j-1)^T    8 fp16 MFMAs, with the softmax of S(j)
+//                                threaded through them and each V fragment
+//                                register refilled with V(j)^T after its MFMA
+//   S(j+1) = K(j+1) Q^T          8 bf16 MFMAs, each K fragment register
+//                                refilled with K(j+2)
+// so that a wave's exponentials run under its own matrix products (vector
+// work of the other wave on the SIMD fills MFMA gaps poorly on this chip).
+// The running max is decided before the stream; a raise rescales O after it,
+// once P(j-1) V(j-1) is in.
+//
+// Ring.  Tiles go from HBM to LDS by direct DMA, three tiles ahead.  Wave w
+// copies the 8 keys that form one MFMA k-group of V: 16-key step w/2, key
+// half w%2, i.e. keys 16 (w/2) + 4 (w%2) + {0..3} and the same + 8.  After
+// its own copies land it converts them alone: transposing reads of its 8 bf16
+// rows give each lane the 8 keys at one head dim, rounded to fp16 and written
+// back over the same 2 KB (dims 0-63 over the first four rows, 64-127 over
+// the second), so a V^T fragment is one 16-byte read.  K stays as copied
+// (16-byte chunks of key k at chunk ^ (k & 15)); V rows are copied with chunk
+// ^ 4 (k & 3) so that the transposing reads are conflict-free.  One workgroup
+// barrier per tile: tile t starts by issuing the DMA of tile t+3 (into the
+// stage of tile t-2, last read in block 2t-3 and consumed before the previous
+// barrier) and ends by waiting for the DMA of tile t+2 and converting it;
+// the barrier then publishes tile t+2, first read in block 2t+2.
 template <int S>
 __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs a) {
     constexpr int NW = 8;
-    constexpr int KT = 64;                          // keys per tile (two 32-key MFMA blocks)
-    constexpr int TILE = KT * kRowBytes;            // bytes of a K (or V) tile
-    constexpr int STAGE = 2 * TILE;                 // K then V
+    constexpr int KT = 64;                 // keys per tile (two 32-key MFMA blocks)
+    constexpr int TILE = KT * kRowBytes;   // bytes of a K (or V) tile
+    constexpr int STAGE = 2 * TILE;        // K then V
     constexpr int RING = S * STAGE;
-    constexpr int ROWS = NW * 32;                   // one 32-row MFMA block per wave
-    constexpr int LD = TILE / (16 * kWave) / NW;    // 16-byte loads per lane per operand
-    static_assert(S == 4, "stage indices below use t & 3");
+    constexpr int ROWS = NW * 32;          // one 32-row MFMA block per wave
+    static_assert(S == 5, "five stages: tiles t-1 .. t+3 are live during tile t");
     static_assert(RING <= 160 * 1024, "LDS budget");
-    static_assert(2 * ROWS * 64 * 4 <= RING, "split-merge scratch fits in the ring");
+    static_assert(2 * ROWS * 64 * 4 + 64 <= RING, "split-merge scratch and its flag fit in the ring");
     __shared__ __attribute__((aligned(1024))) char lds[RING];
-    __shared__ int s_flag;
+    int* const s_flag = reinterpret_cast<int*>(lds + RING - 64);  // used only by the split merge
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -791,256 +800,242 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     if (n_cache < 0) n_cache = 0;
     const int nt = n_cache + ((split == a.nsplit - 1) ? a.tree_tiles : 0);
     const uint32_t ring_addr = (uint32_t)(uintptr_t)(lds_void*)lds;
+    auto stage = [&](int t) { return ring_addr + (uint32_t)(t % S) * STAGE; };
 
-    // This lane moves 16-byte chunks p = (wave LD + i) 64 + lane of a tile:
-    // key p / 16, logical chunk p % 16, stored at chunk ^ (key & 15) for K
-    // and chunk ^ 4 (key & 3) for V.
-    struct Slot {
-        u32x4 k[LD], v[LD];
-    };
-    uint32_t lds_k[LD], lds_v[LD];
+    // ---- this wave's 8 keys of every tile: rows r0 .. r0+3 and r0+8 .. r0+11 ----
+    const int r0 = 16 * (wave >> 1) + 4 * (wave & 1);
+    // DMA of this wave's rows of tile u into stage u % S (1 KB = four rows per
+    // copy).  Past the last tile the last tile is loaded again into the
+    // (free) stage, so that every tile issues the same copies and the wait
+    // counts stay static.  Per-lane byte offsets of a full cache tile's
+    // copies are kept; other tiles recompute them.
+    uint32_t dk[2], dv[2];
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-        const int p = (wave * LD + i) * kWave + lane;
-        const int key = p >> 4, lc = p & 15;
-        lds_k[i] = (uint32_t)(key * kRowBytes + ((lc ^ (key & 15)) << 4));
-        lds_v[i] = (uint32_t)(TILE + key * kRowBytes + ((lc ^ (4 * (key & 3))) << 4));
+    for (int i = 0; i < 2; ++i) {
+        const int key = r0 + 8 * i + (lane >> 4), pc = lane & 15;
+        dk[i] = (uint32_t)(key * kRowBytes + ((pc ^ (key & 15)) << 4));
+        dv[i] = (uint32_t)(key * kRowBytes + ((pc ^ (4 * (key & 3))) << 4));
     }
-    // Loads are issued for every iteration so that the number in flight is
-    // the same on every path (the wait before a slot's store then covers
-    // only that slot); past the last tile the last tile is loaded again
-    // (recently read, so served from cache) and never stored.
-    auto load_tile = [&](int t, Slot& sl) {
-        t = min(t, nt - 1);
-        const char *ks, *vs;
-        uint32_t stride, nk;
-        if (t < n_cache) {
-            const int key0 = (t_begin + t) * KT;
-            const size_t base = ((size_t)bg * a.L + key0) * HD;
-            ks = reinterpret_cast<const char*>(a.Kc + base);
-            vs = reinterpret_cast<const char*>(a.Vc + base);
-            stride = kRowBytes;
-            nk = (uint32_t)min(KT, a.L - key0);
-        } else {
-            const int key0 = (t - n_cache) * KT;
-            const size_t base = ((size_t)(b * a.N + key0) * a.Hkv + g) * HD;
-            ks = reinterpret_cast<const char*>(a.Kt + base);
-            vs = reinterpret_cast<const char*>(a.Vt + base);
-            stride = (uint32_t)a.Hkv * kRowBytes;
-            nk = (uint32_t)min(KT, a.N - key0);
-        }
+    auto issue_dma = [&](int u) {
+        // (uniform selects rather than branches for the source)
+        const int tt = min(u, nt - 1);
+        const bool tree = tt >= n_cache;
+        const int key0 = tree ? (tt - n_cache) * KT : (t_begin + tt) * KT;
+        const size_t base = tree ? ((size_t)(b * a.N + key0) * a.Hkv + g) * HD : ((size_t)bg * a.L + key0) * HD;
+        const char* ks = reinterpret_cast<const char*>((tree ? a.Kt : a.Kc) + base);
+        const char* vs = reinterpret_cast<const char*>((tree ? a.Vt : a.Vc) + base);
+        const uint32_t stride = tree ? (uint32_t)a.Hkv * kRowBytes : (uint32_t)kRowBytes;
+        const int nk = min(KT, (tree ? a.N : a.L) - key0);
+        const uint32_t dst = stage(u) + r0 * kRowBytes;
+        if (!tree && nk == KT) {  // uniform: a full cache tile
 #pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const uint32_t p = (uint32_t)((wave * LD + i) * kWave + lane);
-            const uint32_t key = p >> 4;
-            // ragged tiles repeat their last valid row (masked, finite)
-            const uint32_t off = (key < nk ? key : nk - 1) * stride + ((p & 15) << 4);
-            sl.k[i] = *reinterpret_cast<const u32x4*>(ks + off);
-            sl.v[i] = *reinterpret_cast<const u32x4*>(vs + off);
+            for (int i = 0; i < 2; ++i) {
+                dma16s(ks, dk[i], dst + 8 * i * kRowBytes);
+                dma16s(vs, dv[i], dst + TILE + 8 * i * kRowBytes);
+            }
+            return;
+        }
+        int l = lane;
+        asm volatile("" : "+v"(l));  // recomputed per call rather than held in registers
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int key = r0 + 8 * i + (l >> 4), pc = l & 15;
+            const uint32_t off = (uint32_t)min(key, nk - 1) * stride;  // ragged keys repeat a valid row
+            dma16s(ks, off + ((pc ^ (key & 15)) << 4), dst + 8 * i * kRowBytes);
+            dma16s(vs, off + ((pc ^ (4 * (key & 3))) << 4), dst + TILE + 8 * i * kRowBytes);
         }
     };
-    // V to fp16 (exact bf16 -> fp32, then round to nearest), both halves to LDS
-    auto store_tile = [&](int t, const Slot& sl) {
-        if (t >= nt) return;  // uniform
-        char* st = lds + (t & 3) * STAGE;
+    // In-place conversion of this wave's V rows of tile u.  Transposing read
+    // (dims half hh, rows part p): in each 16-lane group, source lane j reads
+    // row r0 + 8p + j/4 at head dims 64 hh + 16 (lane/16) + 4 (j%4) + {0..3},
+    // so result lane i of the group holds rows r0 + 8p + {0..3} at dim
+    // 64 hh + 16 (lane/16) + i.  The two parts make the lane's 8-key chunk
+    // for that dim, written at row r0 + 8 hh, chunk lane (1 KB per copy).
+    // All reads are issued before the writes over the same bytes.
+    const uint32_t conv_src = (uint32_t)(TILE + (r0 + ((lane & 15) >> 2)) * kRowBytes +
+                                         (((2 * (lane >> 4) + ((lane & 3) >> 1)) ^ (4 * ((lane & 15) >> 2))) << 4) +
+                                         8 * (lane & 1));
+    auto convert = [&](int u) {
+        uint32_t sb = stage(u);
+        asm volatile("" : "+v"(sb));
+        u32x2 part[2][2];  // [dims half][rows part]
 #pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            u32x4 y;
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                y[e] = pack_f16(__uint_as_float(sl.v[i][e] << 16), __uint_as_float(sl.v[i][e] & 0xffff0000u));
-            *reinterpret_cast<u32x4*>(st + lds_k[i]) = sl.k[i];
-            *reinterpret_cast<u32x4*>(st + lds_v[i]) = y;
+            for (int pp = 0; pp < 2; ++pp)
+                // dims half hh is logical chunk ^ 8 hh, so its physical chunk
+                // is the half-0 one ^ 8: address bit 7 (rows and stages are
+                // 256-byte aligned)
+                part[hh][pp] = lds_tr16((sb + conv_src + 8 * pp * kRowBytes) ^ (128 * hh));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = e < 2 ? part[hh][0][e] : part[hh][1][e - 2];
+                w[e] = pack_f16(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
+            }
+            *(lds_u32x4*)(uintptr_t)(sb + TILE + (r0 + 8 * hh) * kRowBytes + lane * 16) = w;
         }
     };
 
-    // LDS offsets within a stage (the generic kernel derives them):
-    //  K fragment (kb, s): (k_off ^ (s << 5)) + 8192 kb
-    //  V^T fragment (step tt, block blk): (v_off ^ (blk << 6)) + 4096 tt (+ 2048 for keys + 8)
+    // fragment reads: K of 32-key block kb of a stage (one 16-byte chunk per
+    // 16 head dims; stage bases are 1 KB aligned, so the xor of bits 5-7
+    // commutes with the add).  V^T of 16-key step h', dims block blk: chunk
+    // of dim 32 blk + n for key half hf, at row 16 h' + 4 hf + 8 (blk/2),
+    // chunk (32 blk + n) % 64.
     const uint32_t k_off = (uint32_t)((n * kRowBytes + hf * 16) ^ ((n & 15) << 4));
-    const int gq = lane >> 4, w16 = lane & 15;
-    const int kr = 4 * (gq >> 1) + (w16 >> 2);
-    const int c0 = 2 * (gq & 1) + ((w16 & 3) >> 1);
-    const uint32_t v_off = (uint32_t)(TILE + ((kr * kRowBytes) | (c0 << 4) | ((kr & 3) << 6)) + 8 * (w16 & 1));
-    uint32_t k_s[8], v_b[4];
+    const uint32_t vt_lane = (uint32_t)(TILE + hf * 4 * kRowBytes + n * 16);
+    bf16x8 kf[8];
+    u32x4 vf[2][4];
+    auto read_k = [&](uint32_t sb, int kb) {
+        const uint32_t ka = sb + 8192 * kb + k_off;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) k_s[s] = k_off ^ (s << 5);
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) v_b[blk] = v_off ^ (blk << 6);
-
-    // per-lane K fragment addresses of a stage (uniform stage base + lane offset)
-    auto k_addrs = [&](uint32_t sb, uint32_t (&ka)[8]) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) ka[s] = sb + k_s[s];
-    };
-    auto read_k = [&](const uint32_t (&ka)[8], int kb, bf16x8 (&kf)[8]) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(bf16x8, lds_ld128(ka[s] + 8192 * kb));
-    };
-    auto qk = [&](const bf16x8 (&kf)[8]) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
-        return acc;
+        for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(bf16x8, lds_ld128(ka ^ (s << 5)));
     };
 
     f32x16 o_acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o_acc[i] = f32x16{};
+    f32x16 s_cur;    // S(j)
+    u32x4 pf[2];     // P(j-1)
     float m_used = -INFINITY;  // raw score units
     float l_run = 0.f;
 
-    // mask (tree / ragged tiles) and lazy running max of one 32-key block;
-    // returns m c for the exponentials.  Element e of the block is key
-    // 8 (e/4) + 4 hf + (e%4).
-    auto softmax_max = [&](auto masked_tag, f32x16& sv, bool is_tree, int key0, int nk, int kb) {
-        if constexpr (decltype(masked_tag)::value) {
+    // block j = 2t + kb of tile t.  V(j)^T is block kb of tile t; K(j+2) is
+    // block kb of tile t+1.
+    auto block = [&](bool masked, int t, int kb) {
+        // (opaque to the compiler, so that the constant parts of the
+        // addresses fold into the instructions' offsets instead of being
+        // precomputed into registers outside the loop)
+        uint32_t sv = stage(t) + 8192 * kb + vt_lane;
+        uint32_t ka = stage(t + 1) + 8192 * kb + k_off;
+        asm volatile("" : "+v"(sv), "+v"(ka));
+        auto pv = [&](int s) {
+            const int h = s >> 2, q = s & 3;
+            o_acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf[h][q]),
+                                                              __builtin_bit_cast(f16x8, pf[h]), o_acc[q], 0, 0, 0);
+            vf[h][q] = lds_ld128(sv + 4096 * h + 2048 * (q >> 1) + 512 * (q & 1));
+        };
+        // two P.V MFMAs depend on nothing computed here: they run under the max
+        pv(0);
+        pv(1);
+        // mask (tree / ragged tiles); element e of the block is key
+        // 8 (e/4) + 4 hf + (e%4).  The tree is one tile (at most 64 nodes),
+        // so block kb of it is word kb of the row's ancestor bits.
+        if (masked) {  // uniform
+            const bool is_tree = t >= n_cache;
+            const int nk = is_tree ? a.N : min(KT, a.L - (t_begin + t) * KT);
             const int kbase = 32 * kb;
             uint32_t vis = nk - kbase >= 32 ? 0xffffffffu : (nk - kbase <= 0 ? 0u : (1u << (nk - kbase)) - 1u);
-            if (is_tree) vis &= (uint32_t)(anc_row >> ((key0 + kbase) & 63));
+            if (is_tree) vis &= (uint32_t)(anc_row >> kbase);
             vis >>= 4 * hf;
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-                if (!((vis >> (8 * (e >> 2) + (e & 3))) & 1u)) sv[e] = -INFINITY;
+                if (!((vis >> (8 * (e >> 2) + (e & 3))) & 1u)) s_cur[e] = -INFINITY;
         }
-        float tmax = fmaxf(sv[0], sv[1]);
+        // lazy running max: raised only when a score exceeds it by 2^kLazyThresh
+        float tmax = fmaxf(s_cur[0], s_cur[1]);
 #pragma unroll
-        for (int e = 2; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sv[e], sv[e + 1]));
+        for (int e = 2; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s_cur[e], s_cur[e + 1]));
         tmax = halves_max(tmax);
         const bool raise = tmax > m_used + kLazyThresh / c || m_used == -INFINITY;
-        if (__ballot(raise)) {
-            const float m_new = raise ? fmaxf(m_used, tmax) : m_used;
-            const float alpha = (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * c);
-            if (raise) {
-                l_run *= alpha;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o_acc[i] *= alpha;
-            }
+        const bool any_raise = __ballot(raise) != 0;
+        float alpha = 1.f;
+        if (raise) {
+            const float m_new = fmaxf(m_used, tmax);
+            alpha = (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * c);
             m_used = m_new;
+            l_run *= alpha;
         }
-        return (m_used == -INFINITY) ? 0.f : m_used * c;
-    };
-    // P = exp2(s c - m c) as fp16 B operands of the block's two 16-key steps
-    auto softmax_exp = [&](const f32x16& sv, float mc, u32x4 (&pf)[2]) {
+        const float mc = (m_used == -INFINITY) ? 0.f : m_used * c;
+
+        // P(j), software-pipelined over score pairs (pair k = elements
+        // 8 (k/4) + 2 (k%4) + {0, 1}): step k issues P.V MFMA k+2, the
+        // exponentials of pair k, the scaling of pair k+1 and the packing and
+        // sum of pair k-1.  The packed pair goes over P(j-1) in place: the
+        // MFMAs reading that half of P(j-1) are issued by then.  The sum uses
+        // the fp16 values handed to the MFMA.
         const f16x2 ones = f16x2{(_Float16)1.f, (_Float16)1.f};
+        float x0 = fmaf(s_cur[0], c, -mc), x1 = fmaf(s_cur[1], c, -mc);
+        float e0 = 0.f, e1 = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t w = pack_f16(__builtin_amdgcn_exp2f(fmaf(sv[8 * h + 2 * q], c, -mc)),
-                                            __builtin_amdgcn_exp2f(fmaf(sv[8 * h + 2 * q + 1], c, -mc)));
-                l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, l_run, false);
-                pf[h][q] = w;
+        for (int k = 0; k <= 8; ++k) {
+            if (k + 2 < 8) pv(k + 2);
+            float n0 = 0.f, n1 = 0.f;
+            if (k < 8) {
+                n0 = __builtin_amdgcn_exp2f(x0);
+                n1 = __builtin_amdgcn_exp2f(x1);
             }
-    };
-    // V^T fragments of 16-key step h of block kb
-    auto read_v = [&](const uint32_t (&va)[4], int kb, int h, u32x2 (&vl)[4], u32x2 (&vh)[4]) {
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            vl[blk] = lds_tr16(va[blk] + 4096 * (2 * kb + h));
-            vh[blk] = lds_tr16(va[blk] + 4096 * (2 * kb + h) + 2048);
+            if (k + 1 < 8) {
+                const int e = 8 * ((k + 1) >> 2) + 2 * ((k + 1) & 3);
+                x0 = fmaf(s_cur[e], c, -mc);
+                x1 = fmaf(s_cur[e + 1], c, -mc);
+            }
+            if (k >= 1) {
+                uint32_t w = pack_f16(e0, e1);
+                asm volatile("" : "+v"(w));  // packed here, not sunk to its use in the next block
+                l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, l_run, false);
+                pf[(k - 1) >> 2][(k - 1) & 3] = w;
+            }
+            e0 = n0;
+            e1 = n1;
+            __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    auto pv = [&](const u32x2 (&vl)[4], const u32x2 (&vh)[4], const u32x4& p) {
+        // S(j) is dead: S(j+1) takes its registers
+        f32x16 s_next = f32x16{};
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-            o_acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, u32x4{vl[blk].x, vl[blk].y, vh[blk].x, vh[blk].y}),
-                __builtin_bit_cast(f16x8, p), o_acc[blk], 0, 0, 0);
-    };
-    // scheduling: the eight score MFMAs of the next block each followed by
-    // six vector-ALU instructions of the current block's exponentials
-    auto interleave_qk_exp = [&]() {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        for (int s = 0; s < 8; ++s) {
+            s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], s_next, 0, 0, 0);
+            kf[s] = __builtin_bit_cast(bf16x8, lds_ld128(ka ^ (s << 5)));
         }
-    };
-
-    uint32_t sb = ring_addr;  // stage base of tile t (uniform)
-    uint32_t ka[8];           // K fragment addresses of tile t
-    f32x16 s_a;               // scores of block 0 of tile t
-
-    // one tile; `ld` receives tile t+3, `st` holds tile t+2.  Tiles that need
-    // the mask (tree tiles, a ragged last tile) run a separate instance.
-    auto iteration = [&](auto masked_tag, int t, Slot& ld, Slot& st) {
-        const bool is_tree = t >= n_cache;
-        const int key0 = is_tree ? (t - n_cache) * KT : (t_begin + t) * KT;
-        const int nk = is_tree ? min(KT, a.N - key0) : min(KT, a.L - key0);
-        u32x4 pf[2];
-        u32x2 vl[2][4], vh[2][4];
-        bf16x8 kf[8];
-        uint32_t va[4];
+        // a raise rescales everything accumulated so far, P(j-1) V(j-1) included
+        if (any_raise) {
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) va[blk] = sb + v_b[blk];
-        const uint32_t sb_next = sb + STAGE == ring_addr + RING ? ring_addr : sb + STAGE;
-        // step 1
-        read_k(ka, 1, kf);
-        float mc = softmax_max(masked_tag, s_a, is_tree, key0, nk, 0);
-        f32x16 s_b = qk(kf);
-        softmax_exp(s_a, mc, pf);
-        interleave_qk_exp();
-        load_tile(t + 3, ld);
-        // step 2
-        // (the P.V steps run at raised wave priority: the SIMD's other wave is
-        // then in its exponentials, which fill the MFMA gaps)
-        __builtin_amdgcn_s_setprio(1);
-        read_v(va, 0, 0, vl[0], vh[0]);
-        read_v(va, 0, 1, vl[1], vh[1]);
-        store_tile(t + 2, st);
-        pv(vl[0], vh[0], pf[0]);
-        pv(vl[1], vh[1], pf[1]);
-        __builtin_amdgcn_s_setprio(0);
-        // step 3
-        __syncthreads();
-        // step 4 (past the last tile the scores come from a stage no tile
-        // uses and are dropped)
-        k_addrs(sb_next, ka);
-        read_k(ka, 0, kf);
-        mc = softmax_max(masked_tag, s_b, is_tree, key0, nk, 1);
-        s_a = qk(kf);
-        softmax_exp(s_b, mc, pf);
-        interleave_qk_exp();
-        // step 5
-        __builtin_amdgcn_s_setprio(1);
-        read_v(va, 1, 0, vl[0], vh[0]);
-        read_v(va, 1, 1, vl[1], vh[1]);
-        pv(vl[0], vh[0], pf[0]);
-        pv(vl[1], vh[1], pf[1]);
-        __builtin_amdgcn_s_setprio(0);
-        sb = sb_next;
+            for (int i = 0; i < 4; ++i) o_acc[i] *= alpha;
+        }
+        s_cur = s_next;
     };
 
-    // ---- prologue: tiles 0 and 1 in LDS, tile 2 in flight ----
-    Slot s0, s1;
-    load_tile(0, s0);
-    load_tile(1, s1);
-    store_tile(0, s0);
-    store_tile(1, s1);
-    load_tile(2, s0);
-    __syncthreads();
-    k_addrs(sb, ka);
+    // ---- prologue: DMA of tiles 0-2; tiles 0 and 1 converted; S(0); K(1)
+    // in registers; P(-1) = 0 with finite V(-1) ----
+#pragma unroll
+    for (int u = 0; u < 3; ++u) issue_dma(u);
+    wait_vmcnt<4>();  // tiles 0 and 1 have landed
+    convert(0);
+    convert(1);
+    __syncthreads();  // tiles 0 and 1 are visible
+    read_k(ring_addr, 0);
     {
-        bf16x8 kf[8];
-        read_k(ka, 0, kf);
-        s_a = qk(kf);
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
+        s_cur = acc;
     }
-    // full cache tiles (no mask) in pairs, so that the slots alternate
-    // statically; then the rest (a ragged last cache tile, the tree tiles and
-    // an odd leftover) with the mask
+    read_k(ring_addr, 1);
+    pf[0] = pf[1] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) vf[h][blk] = u32x4{0, 0, 0, 0};
+
     const int n_full = (t_begin + n_cache) * KT <= a.L ? n_cache : n_cache - 1;
-    int t = 0;
-    for (; t + 1 < n_full; t += 2) {
-        iteration(Flag<false>{}, t, s1, s0);
-        iteration(Flag<false>{}, t + 1, s0, s1);
+    for (int t = 0; t < nt; ++t) {
+        const bool masked = t >= n_full;  // tree tiles and a ragged last cache tile
+        issue_dma(t + 3);
+        block(masked, t, 0);
+        block(masked, t, 1);
+        wait_vmcnt<4>();  // tile t+2 has landed (tile t+3 still in flight)
+        convert(t + 2);
+        __syncthreads();  // tile t+2 is visible; tile t-1's last reads are consumed
     }
-    for (; t < nt; ++t) {
-        iteration(Flag<true>{}, t, s1, s0);
-        const Slot tmp_slot = s0;  // the slot roles alternate
-        s0 = s1;
-        s1 = tmp_slot;
-    }
+    // the last block's P.V
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        o_acc[s & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf[s >> 2][s & 3]),
+                                                              __builtin_bit_cast(f16x8, pf[s >> 2]), o_acc[s & 3], 0,
+                                                              0, 0);
+    wait_vmcnt<0>();  // no copy into this workgroup's LDS outlives it
 
     const float l_tot = halves_sum(l_run);
     const float m_log = (m_used == -INFINITY) ? -INFINITY : m_used * c;  // log2 units from here on
@@ -1077,7 +1072,7 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
             st_dev_f(a.part_ml + prow * 2 + 1, l_tot);
         }
     }
-    merge_splits<64 * NW, ROWS>(a, lds, &s_flag, grp, row0, nrows, b, g);
+    merge_splits<64 * NW, ROWS>(a, lds, s_flag, grp, row0, nrows, b, g);
 }
 
 }  // namespace
@@ -1151,7 +1146,7 @@ extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, con
             hipLaunchKernelGGL((tree_attention_kernel<2, 64, 2, 2, 4>), dim3(a.nblocks), dim3(256), 0, st, a);
             break;
         default:
-            hipLaunchKernelGGL((tree_attention_wide_kernel<4>), dim3(a.nblocks), dim3(512), 0, st, a);
+            hipLaunchKernelGGL((tree_attention_wide_kernel<5>), dim3(a.nblocks), dim3(512), 0, st, a);
             break;
     }
     return launch_status();
