@@ -169,6 +169,41 @@ def copy_calibration(torch, dev, nbytes=COPY_CAL_BYTES):
     del src, dst
 
 
+def achievable_peaks(torch, dev, stream):
+    """The device's reachable rates in this run, beside the spec peaks: a
+    streaming read (torch row sums over 2 GiB of fp32, 262144 rows of 2 KiB),
+    a plain copy (512 MiB read plus 512 MiB written) and a library bf16 GEMM
+    (torch.matmul, 16384^3)."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1e3  # seconds per call
+    out = {}
+    big = torch.ones((2 << 30) // 4, dtype=torch.float32, device=dev)
+    rows = big.view(262144, -1)
+    out["hbm_read_GB/s"] = round(big.numel() * 4 / timed(lambda: rows.sum(1), 5) / 1e9, 1)
+    del rows
+    del big
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    out["copy_GB/s"] = round(2 * COPY_CAL_BYTES / timed(lambda: dst.copy_(src), 10) / 1e9, 1)
+    del src, dst
+    n = 16384
+    x = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    y = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    out["bf16_gemm_TFLOP/s"] = round(2 * n ** 3 / timed(lambda: torch.matmul(x, y), 3) / 1e12, 1)
+    del x, y
+    torch.cuda.synchronize()
+    return out
+
+
 def kernel_sources_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -326,6 +361,10 @@ def main():
                 "algorithmic_bytes": c_bytes, "avg_us": round(per["accept"] * 1e3, 3)}
         roof["traffic"] = counted_traffic(w.name, "spec_accept_kernel<false, true>", ACC_SOURCES)
 
+    peaks = achievable_peaks(torch, dev, stream)
+    reach = peaks["bf16_gemm_TFLOP/s"] if roof["unit"] == "TFLOP/s" else peaks["hbm_read_GB/s"]
+    roof["frac_of_achievable"] = round(roof["achieved"] / reach, 4)
+
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -351,6 +390,7 @@ def main():
         "accept": {"GB/s": round(acc_gbs, 1), "hbm_frac": round(acc_gbs / HBM_PEAK_GBS, 4),
                    "greedy_GB/s": round(accept_bytes(w, True) / (per_g["accept_greedy"] / 1e3) / 1e9, 1)},
         "greedy": {"value": round(nodes / (ms_greedy / 1e3), 1), "ms_per_step": round(ms_greedy, 5)},
+        "achievable": peaks,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, first_inputs, T, args.cpu_seconds)
