@@ -304,6 +304,31 @@ def test_accept_edge_cases(tv):
     assert a.numel() == 0
 
 
+def test_accept_invalid_trees_between_valid_ones(tv):
+    """Teams of several members that verify several sequences each (B above
+    the teams the device holds at once), with an invalid tree between valid
+    ones: every valid sequence matches the oracle and every invalid one is
+    reported as such."""
+    B, N, V = 160, 4, 131072  # V needs >= 4 members per team; 64 teams then hold three sequences each
+    rng = np.random.default_rng(11)
+    q = rng.normal(0, 3, size=(B, N, V)).astype(np.float32)
+    p = (q[:, [0, 0, 1, 2]] + rng.normal(0, 1, size=(B, N, V))).astype(np.float32)
+    draft = p.argmax(-1).astype(np.int32)
+    par = np.tile(chain(N), (B, 1)).astype(np.int32)
+    bad = np.arange(B)[(np.arange(B) >= 64) & (np.arange(B) < 128)]
+    par[bad, 2] = 3  # parent after the node: invalid
+    tq, tp, td, tpar = (torch.from_numpy(x).to(dev()) for x in (q, p, draft, par))
+    ok = np.setdiff1d(np.arange(B), bad)
+    # the valid sequences against the oracle on the same batch with every tree valid (the walk's
+    # uniforms are keyed by the sequence index, so the batch keeps its numbering)
+    good_par = np.tile(chain(N), (B, 1)).astype(np.int32)
+    for greedy in (True, False):
+        a, n, t = _accept_gpu(tv, tq, None if greedy else tp, td, tpar, 3, 1.0, greedy)
+        assert (a[bad] == -1).all() and (t[bad] == -1).all() and (n[bad] == -1).all()
+        ref = oracle.spec_accept(q, None if greedy else p, draft, good_par, seed=3, temperature=1.0, greedy=greedy)
+        _compare_walk((a[ok], n[ok], t[ok]), {k: np.asarray(v)[ok] for k, v in ref.items()}, greedy)
+
+
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_accept_full_config(tv, name):
     w = CONFIGS[name]

@@ -649,7 +649,11 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
         int32_t* out_nodes = a.accepted + (size_t)b * N;
         int32_t* out_toks = a.tokens + (size_t)b * N;
         if (!s_ok) {
-            // every member sees the same tree: nobody streams or synchronises
+            // every member sees the same tree: nobody streams or synchronises.
+            // The sequence takes no statistics buffer (iter does not advance):
+            // the next one reuses the buffer this one would have taken, so a
+            // member never overwrites entries of the sequence before the last
+            // one it merged, which another member may still be merging.
             if (w == 0) {
                 if (tid == 0) a.accept_len[b] = -1;
                 for (int i = tid; i < N; i += kThreads) {
@@ -658,6 +662,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 }
             }
             __syncthreads();
+            --iter;
             continue;
         }
 
