@@ -132,7 +132,9 @@ int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t
  *   p_logits     fp32 [B,N,V]  row c = draft logits that produced node c (row 0
  *                              unused).  May be NULL when greedy.
  *   draft_tokens int32 [B,N]   token of node c (entry 0 ignored); each in [0,V).
- *   parent       int32 [B,N]   the tree; must be valid (see tv_build_tree_mask).
+ *   parent       int32 [B,N]   the tree (conventions above).  It is checked on
+ *                              the device: a sequence whose parent[] breaks them
+ *                              gets accept_len -1 and -1 in both outputs.
  *   philox_seed  key of the Philox-4x32-10 uniforms: the accept test of node c
  *                in sequence b uses counter (c, b, 0, 0), the final draw after
  *                stopping at node u uses (u, b, 1, 0); U = (word0 >> 8) * 2^-24.
