@@ -171,28 +171,19 @@ __device__ __forceinline__ double block_scan_d(double v, double* wt, double& exc
     return pre + v;
 }
 
-// The same scan with one barrier: the caller guarantees that a workgroup
-// barrier separates every earlier read of `wt` from this call (the walk
-// alternates two such arrays between its two scans per step).
-__device__ __forceinline__ double block_scan_1b(double v, double* wt, double& excl, double& tot) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double y = __shfl_up(v, o);
-        if (lane >= o) v += y;
-    }
-    const double prev = __shfl_up(v, 1);
-    if (lane == kWave - 1) wt[wave] = v;
+// Block sum in fp64 with one barrier: a DPP reduction per wave, then the wave
+// totals in order (a fixed association, identical on every member).  The
+// caller guarantees that a workgroup barrier separates every earlier read of
+// `wt` from this call (the walk alternates two such arrays between its two
+// sums per step).
+__device__ __forceinline__ double block_sum_1b(double v, double* wt) {
+    v = group_sum_dpp(v, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) wt[threadIdx.x >> 6] = v;
     __syncthreads();
-    double pre = 0.0, t = 0.0;
+    double t = 0.0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        if (i < wave) pre += wt[i];
-        t += wt[i];
-    }
-    tot = t;
-    excl = lane == 0 ? pre : pre + prev;
-    return pre + v;
+    for (int i = 0; i < kWaves; ++i) t += wt[i];
+    return t;
 }
 
 // Larger value wins; equal values go to the smaller index.
@@ -625,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
     // sampling: the member's slice of the current residual
     __shared__ __attribute__((aligned(16))) float s_res[GREEDY ? 4 : kMaxSlice];
     __shared__ double s_wt[kWaves];
-    __shared__ double s_wtw[2][GREEDY ? 1 : kWaves];  // the walk's two scans per step
+    __shared__ double s_wtw[2][GREEDY ? 1 : kWaves];  // the walk's two sums per step
     __shared__ double s_mass[GREEDY ? 1 : kMaxTeamSize];
     __shared__ double s_tab[32];
     __shared__ double s_rejZ[GREEDY ? 1 : TV_MAX_NODES];
@@ -788,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 // ---- 4. rejected: residual pass over the slices.  Only the member
                 // that owns the next sibling's token publishes words 2 and 3 that
                 // anyone reads, and its pass always writes them (x2l is in its
-                // slice), so s_wx needs no reset.  Barriers: the two scans (each on
+                // slice), so s_wx needs no reset.  Barriers: the two sums (each on
                 // its own array, so no leading barrier) ----
                 int nxt = cc + 1;
                 while (nxt < N && s_par[nxt] != u) ++nxt;
@@ -801,8 +792,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 const double part = residual_pass<VEC4>(res_active ? nullptr : q_u, pb + (size_t)cc * V + s0, Mq,
                                                         invSq, s_M[N + cc], (float)(1.0 / s_S[N + cc]), invZ, c,
                                                         nsl, s_res, x2l, &s_wx[1], &s_wx[0]);
-                double sexcl, smass;
-                block_scan_1b(part, s_wtw[0], sexcl, smass);  // its barrier publishes s_wx
+                const double smass = block_sum_1b(part, s_wtw[0]);  // its barrier publishes s_wx
                 // publish and gather in one step: every word carries the step's tag,
                 // so a member polls the other members' words directly
                 uint64_t* slot = reinterpret_cast<uint64_t*>(massb + (size_t)pass * W * kMassRec);
@@ -826,8 +816,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                         s_nwx[1] = __uint_as_float((uint32_t)e[3]);
                     }
                 }
-                double mexcl, Znew;
-                block_scan_1b(mt, s_wtw[1], mexcl, Znew);  // its barrier publishes s_nwx
+                const double Znew = block_sum_1b(mt, s_wtw[1]);  // its barrier publishes s_nwx
                 ++pass;
                 if (Znew > 0.0) {
                     if (tid < W) s_mass[tid] = mt;
