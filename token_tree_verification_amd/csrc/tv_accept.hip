@@ -358,22 +358,27 @@ __device__ __forceinline__ int lanes_per_row(int W) {
 // Statistics entries are two tagged words, (tag, first value) and (tag, second
 // value); a merge polls them until every word carries the sequence's tag, so
 // no team barrier separates the stream from the merge.  Lanes whose entries
-// are not yet published load them again.
-constexpr int kBatch = 1;
-
-template <int K>
-__device__ __forceinline__ void poll_entries(const uint64_t* stats, const uint32_t (&idx)[K][4], uint64_t tg,
-                                             uint64_t (&e)[K][4][2], uint64_t* line) {
+// are not yet published load them again.  A lane covers PER members of a row
+// (lanes_per_row(W) lanes per row) and issues the loads of KB row groups
+// before it waits.  Teams of up to 64 members take one member per lane and
+// four groups, so one round trip covers 4096 / lanes_per_row(W) rows (every
+// row of a 64-node tree for teams of up to 32); larger teams take four
+// members per lane and one group (16 rows per round trip).
+template <int KB, int PER>
+__device__ __forceinline__ void poll_entries(const uint64_t* stats, const uint32_t (&idx)[KB][PER], int nk, uint64_t tg,
+                                             uint64_t (&e)[KB][PER][2], uint64_t* line) {
     auto fetch = [&]() {
         bool ok = true;
 #pragma unroll
-        for (int k = 0; k < K; ++k)
+        for (int k = 0; k < KB; ++k) {
+            if (k >= nk) break;  // wave-uniform
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < PER; ++i) {
                 e[k][i][0] = ld_dev(&stats[2 * (size_t)idx[k][i]]);
                 e[k][i][1] = ld_dev(&stats[2 * (size_t)idx[k][i] + 1]);
                 ok = ok && (e[k][i][0] & 0xffffffff00000000ull) == tg && (e[k][i][1] & 0xffffffff00000000ull) == tg;
             }
+        }
         return ok;
     };
     bool ok = fetch();
@@ -388,42 +393,58 @@ __device__ __forceinline__ void poll_entries(const uint64_t* stats, const uint32
     }
 }
 
-// Sampling: merged max sM[r] and normaliser sS[r] = sum_w s_w exp((m_w - M)/T)
-// of every streamed row, from the entries [r][W].  Each wave issues the loads
-// of kBatch row groups before reducing any of them.  The factors are fp32
-// (relative error ~1e-7), the sums fp64.
+// Row groups of a merge pass: group k of wave w starts at row
+// base + (k kWaves + w) rpw, so every wave takes a group before any takes a
+// second; a wave's groups past the last row are skipped (nk counts the
+// others).  Entry indices are r W + member (< 2^15), with rows past the last
+// and members past W clamped so that the loads stay unconditional.
+template <int KB, int PER>
+__device__ __forceinline__ int entry_indices(int base, int wave, int rpw, int g, int li, int lpr, int nrows, int N,
+                                             int W, bool storage_rows, uint32_t (&idx)[KB][PER]) {
+    int nk = 0;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        const int r0 = base + (k * kWaves + wave) * rpw;
+        if (r0 < nrows) nk = k + 1;
+        const int ri = min(r0 + g, nrows - 1);
+        const int r = storage_rows ? stat_row(ri, N) : ri;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) idx[k][i] = (uint32_t)(r * W + min(li + lpr * i, W - 1));
+    }
+    return nk;
+}
 
-__device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows, int N, int W, float c, float* sM,
-                                               double* sS, uint64_t tg, uint64_t* line) {
+// Sampling: merged max sM[r] and normaliser sS[r] = sum_w s_w exp((m_w - M)/T)
+// of every streamed row, from the entries [r][W].  The factors are fp32
+// (relative error ~1e-7), the sums fp64.
+template <int KB, int PER>
+__device__ __forceinline__ void merge_sampling_t(const uint64_t* stats, int nrows, int N, int W, float c, float* sM,
+                                                 double* sS, uint64_t tg, uint64_t* line) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lpr = lanes_per_row(W);
-    const int rpw = kWave / lpr;              // rows per wave per group
-    const int per = (W + lpr - 1) / lpr;      // members per lane (<= 4)
+    const int rpw = kWave / lpr;  // rows per wave per group
     const int g = lane / lpr, li = lane % lpr;
-    for (int r0 = wave * rpw * kBatch; r0 < nrows; r0 += kWaves * rpw * kBatch) {
-        // loads are unconditional (indices clamped) so that they all stay in flight
-        uint32_t idx[kBatch][4];  // entry index r W + member (< 2^15)
+    for (int base = 0; base < nrows; base += KB * kWaves * rpw) {
+        uint32_t idx[KB][PER];
+        const int nk = entry_indices<KB, PER>(base, wave, rpw, g, li, lpr, nrows, N, W, true, idx);
+        if (nk == 0) break;
+        uint64_t e[KB][PER][2];
+        poll_entries<KB, PER>(stats, idx, nk, tg, e, line);
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int ri = r0 + k * rpw + g;
-            const int r = stat_row(min(ri, nrows - 1), N);
+        for (int k = 0; k < KB; ++k) {
+            if (k >= nk) break;
+            const int ri = base + (k * kWaves + wave) * rpw + g;
+            float mk[PER];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) idx[k][i] = (uint32_t)(r * W + min(li + lpr * i, W - 1));
-        }
-        uint64_t e[kBatch][4][2];
-        poll_entries<kBatch>(stats, idx, tg, e, line);
+            for (int i = 0; i < PER; ++i) mk[i] = li + lpr * i < W ? lo_f(e[k][i][0]) : -INFINITY;
+            float M = mk[0];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int ri = r0 + k * rpw + g;
-            float mk[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mk[i] = (i < per && li + lpr * i < W) ? lo_f(e[k][i][0]) : -INFINITY;
-            float M = fmaxf(fmaxf(mk[0], mk[1]), fmaxf(mk[2], mk[3]));
+            for (int i = 1; i < PER; ++i) M = fmaxf(M, mk[i]);
             M = group_max_dpp(M, lpr);
             double S = 0.0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < PER; ++i)
                 if (mk[i] != -INFINITY) S += (double)lo_f(e[k][i][1]) * (double)__builtin_amdgcn_exp2f((mk[i] - M) * c);
             S = group_sum_dpp(S, lpr);
             if (ri < nrows && li == 0) {
@@ -435,37 +456,50 @@ __device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows,
     }
 }
 
+__device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows, int N, int W, float c, float* sM,
+                                               double* sS, uint64_t tg, uint64_t* line) {
+    if (W <= kWave)
+        merge_sampling_t<4, 1>(stats, nrows, N, W, c, sM, sS, tg, line);
+    else
+        merge_sampling_t<1, kMaxTeamSize / kWave>(stats, nrows, N, W, c, sM, sS, tg, line);
+}
+
 // Greedy: argmax of every target row 0..N-1 from the entries [r][W].
-__device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W, int* amax, uint64_t tg,
-                                             uint64_t* line) {
+template <int KB, int PER>
+__device__ __forceinline__ void merge_greedy_t(const uint64_t* stats, int N, int W, int* amax, uint64_t tg,
+                                               uint64_t* line) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lpr = lanes_per_row(W);
     const int rpw = kWave / lpr;
-    const int per = (W + lpr - 1) / lpr;
     const int g = lane / lpr, li = lane % lpr;
-    for (int r0 = wave * rpw * kBatch; r0 < N; r0 += kWaves * rpw * kBatch) {
-        uint32_t idx[kBatch][4];  // entry index r W + member (< 2^15)
+    for (int base = 0; base < N; base += KB * kWaves * rpw) {
+        uint32_t idx[KB][PER];
+        const int nk = entry_indices<KB, PER>(base, wave, rpw, g, li, lpr, N, N, W, false, idx);
+        if (nk == 0) break;
+        uint64_t e[KB][PER][2];
+        poll_entries<KB, PER>(stats, idx, nk, tg, e, line);
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int r = min(r0 + k * rpw + g, N - 1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) idx[k][i] = (uint32_t)(r * W + min(li + lpr * i, W - 1));
-        }
-        uint64_t e[kBatch][4][2];
-        poll_entries<kBatch>(stats, idx, tg, e, line);
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int r = r0 + k * rpw + g;
+        for (int k = 0; k < KB; ++k) {
+            if (k >= nk) break;
+            const int r = base + (k * kWaves + wave) * rpw + g;
             float bv = -INFINITY;
             int bi = 0x7fffffff;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i < per && li + lpr * i < W) argmax_merge(bv, bi, lo_f(e[k][i][0]), (int)(uint32_t)e[k][i][1]);
+            for (int i = 0; i < PER; ++i)
+                if (li + lpr * i < W) argmax_merge(bv, bi, lo_f(e[k][i][0]), (int)(uint32_t)e[k][i][1]);
             group_argmax_dpp(bv, bi, lpr);
             if (r < N && li == 0) amax[r] = bi;
         }
     }
+}
+
+__device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W, int* amax, uint64_t tg,
+                                             uint64_t* line) {
+    if (W <= kWave)
+        merge_greedy_t<4, 1>(stats, N, W, amax, tg, line);
+    else
+        merge_greedy_t<1, kMaxTeamSize / kWave>(stats, N, W, amax, tg, line);
 }
 
 // --------------------------------------------------------- residual passes --
