@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 COPY_CAL_BYTES = 512 << 20
+PROBE_LIB = os.path.join(ROOT, "token_tree_verification_amd", "libtv_probe.so")
 ATTN_SOURCES = ("token_tree_verification_amd/csrc/tv_attention.hip", "token_tree_verification_amd/csrc/tv_device.h")
 ACC_SOURCES = ("token_tree_verification_amd/csrc/tv_accept.hip", "token_tree_verification_amd/csrc/tv_device.h")
 
@@ -170,10 +171,12 @@ def copy_calibration(torch, dev, nbytes=COPY_CAL_BYTES):
 
 
 def achievable_peaks(torch, dev, stream):
-    """The device's reachable rates in this run, beside the spec peaks: a
-    streaming read (torch row sums over 2 GiB of fp32, 262144 rows of 2 KiB),
-    a plain copy (512 MiB read plus 512 MiB written) and a library bf16 GEMM
-    (torch.matmul, 16384^3)."""
+    """The device's reachable rates in this run, beside the spec peaks: the
+    probe library's streaming read (2 GiB of 16-byte loads, a contiguous range
+    per workgroup) and pure MFMA loop
+    (four independent v_mfma_f32_32x32x16_bf16 chains per wave, four waves per
+    SIMD), a plain copy (512 MiB read plus 512 MiB written) and a library bf16
+    GEMM (torch.matmul, 16384^3)."""
     def timed(fn, reps):
         fn()
         torch.cuda.synchronize()
@@ -185,12 +188,30 @@ def achievable_peaks(torch, dev, stream):
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps / 1e3  # seconds per call
+    probe = ctypes.CDLL(PROBE_LIB)
+    probe.tv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
+    probe.tv_probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.tv_probe_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    probe.tv_probe_mfma_loop_flops.restype = ctypes.c_double
+    st = ctypes.c_void_p(stream.cuda_stream)
+
+    def call(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe call failed ({rc})")
+
     out = {}
+    nblk = 2048  # the fastest of 512 .. 16384 workgroups on this device
+    sink = torch.empty(4096 * 256, dtype=torch.float32, device=dev)
     big = torch.ones((2 << 30) // 4, dtype=torch.float32, device=dev)
-    rows = big.view(262144, -1)
-    out["hbm_read_GB/s"] = round(big.numel() * 4 / timed(lambda: rows.sum(1), 5) / 1e9, 1)
-    del rows
+    t = timed(lambda: call(probe.tv_probe_stream_read(ctypes.c_void_p(big.data_ptr()), big.numel() * 4,
+                                                      ctypes.c_void_p(sink.data_ptr()), nblk, st)), 5)
+    out["hbm_read_GB/s"] = round(big.numel() * 4 / t / 1e9, 1)
     del big
+    mblk, iters = 1024, 4096  # four workgroups of four waves per CU
+    t = timed(lambda: call(probe.tv_probe_mfma_loop(mblk, iters, ctypes.c_void_p(sink.data_ptr()), st)), 3)
+    out["mfma_loop_bf16_TFLOP/s"] = round(probe.tv_probe_mfma_loop_flops(mblk, iters) / t / 1e12, 1)
+    del sink
     src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     out["copy_GB/s"] = round(2 * COPY_CAL_BYTES / timed(lambda: dst.copy_(src), 10) / 1e9, 1)
@@ -362,7 +383,7 @@ def main():
         roof["traffic"] = counted_traffic(w.name, "spec_accept_kernel<false, true>", ACC_SOURCES)
 
     peaks = achievable_peaks(torch, dev, stream)
-    reach = peaks["bf16_gemm_TFLOP/s"] if roof["unit"] == "TFLOP/s" else peaks["hbm_read_GB/s"]
+    reach = peaks["mfma_loop_bf16_TFLOP/s"] if roof["unit"] == "TFLOP/s" else peaks["hbm_read_GB/s"]
     roof["frac_of_achievable"] = round(roof["achieved"] / reach, 4)
 
     res = {

@@ -117,3 +117,40 @@ def test_python_binding_rejects_host_tensors():
         tv.build_tree_mask(torch.zeros((1, 3), dtype=torch.int32))
     with pytest.raises(TypeError):
         tv.build_tree_mask(torch.zeros((1, 3), dtype=torch.int64))
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "tv_probe.h")
+
+
+@pytest.fixture(scope="module")
+def probe():
+    path = os.path.join(ROOT, "token_tree_verification_amd", "libtv_probe.so")
+    if not os.path.exists(path):
+        from token_tree_verification_amd import build as tvbuild
+        tvbuild.build_probe()
+    return ctypes.CDLL(path)
+
+
+def test_probe_library_exports_its_header(probe):
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(tv_probe_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["tv_probe_mfma_loop", "tv_probe_mfma_loop_flops", "tv_probe_stream_read"]
+    for name in names:
+        assert hasattr(probe, name), name
+
+
+def test_probe_host_checks(probe):
+    probe.tv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
+    probe.tv_probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.tv_probe_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    probe.tv_probe_mfma_loop_flops.restype = ctypes.c_double
+    assert probe.tv_probe_stream_read(None, 1 << 20, 16, 8, None) == -1        # null source
+    assert probe.tv_probe_stream_read(16, 8, 16, 8, None) == -1                # fewer than 16 bytes
+    assert probe.tv_probe_stream_read(24, 1 << 20, 16, 8, None) == -1          # misaligned source
+    assert probe.tv_probe_stream_read(16, 1 << 20, 16, 0, None) == -1          # no workgroups
+    assert probe.tv_probe_mfma_loop(0, 8, 16, None) == -1
+    assert probe.tv_probe_mfma_loop(8, 0, 16, None) == -1
+    assert probe.tv_probe_mfma_loop(8, 8, None, None) == -1
+    # 32 x 32 x 16 multiply-adds per MFMA, four chains, four waves per workgroup
+    assert probe.tv_probe_mfma_loop_flops(3, 5) == 2 * 32 * 32 * 16 * 4 * 5 * 4 * 3

@@ -1,5 +1,5 @@
-"""Static checks on the gfx950 code of every libtv kernel (CPU only; hipcc
-cross-compiles):
+"""Static checks on the gfx950 code of every libtv kernel and of the
+measurement probes (CPU only; hipcc cross-compiles):
 
 * no kernel reads the dispatch packet (it lives in host memory; a compiler
   that promotes dynamically indexed private arrays to LDS reads the
@@ -31,6 +31,7 @@ def _asm(src, d):
 @pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
 def test_kernel_resources():
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    srcs.append(os.path.join(ROOT, "token_tree_verification_amd", "probe", "tv_probe.hip"))
     with tempfile.TemporaryDirectory() as d:
         for src in srcs:
             text = _asm(src, d)

@@ -11,6 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtv.so")
+PROBE_SRC = os.path.join(HERE, "probe", "tv_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libtv_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -74,7 +76,23 @@ def build(verbose: bool = False) -> str:
         if res.returncode != 0:
             raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the measurement probes (plain streaming-read and MFMA-loop
+    kernels) into token_tree_verification_amd/libtv_probe.so."""
+    tmp = PROBE_LIB + f".tmp{os.getpid()}"
+    cmd = ["hipcc", *HIPCC_FLAGS, "-I", INCLUDE, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        err = "\n".join(l for l in (res.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
