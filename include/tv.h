@@ -104,8 +104,8 @@ int tv_build_tree_mask(const int32_t* parent, int B, int N, uint64_t* anc_mask, 
  * P and V in fp16 and fp32 accumulation.  Precondition: |V| <= 65504.
  * Workspace: at least tv_tree_attention_workspace(...) bytes, 256-byte aligned
  * (may be NULL when that size is 0), zero-filled before its first use: when the
- * cache is split across workgroups it holds their partial results and two
- * counters per row tile, which the call returns to zero before it ends.
+ * cache is split across workgroups it holds their partial results and one
+ * arrival counter per row tile, which the last workgroup resets to zero.
  * Calls that share a workspace must not overlap.
  */
 size_t tv_tree_attention_workspace(int B, int N, int Hq, int Hkv, int D, int L);

@@ -46,8 +46,6 @@
 //    the same XCD (same L2).
 #include <float.h>
 
-#include <mutex>
-
 #include "tv_device.h"
 #include "tv_internal.h"
 
@@ -58,7 +56,6 @@ constexpr int HD = TV_HEAD_DIM;
 constexpr int kRowBytes = HD * 2;            // one key row of K or V (bf16)
 constexpr int kTargetWorkgroups = 256;   // one per CU (a workgroup fills a CU)
 constexpr int kBalance = 1;              // splits beyond kBalance * sqrt(L / R) are not worth their merge
-constexpr uint32_t kMergeSpinLimit = 1u << 22;  // bound on the shared merge's wait (polls of ~1 us)
 constexpr float kLazyThresh = 8.f;           // log2 units the running max may lag the true max
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -75,10 +72,8 @@ struct AttnArgs {
     float* part_o;     // [groups][nsplit][rows per tile][HD]
     float* part_ml;    // [groups][nsplit][rows per tile][2]
     uint32_t* counter; // [groups], zero between calls
-    uint32_t* done;    // [groups], zero between calls (the shared merge)
     int N, Hq, Hkv, G, L, R;
     int row_tiles, nsplit, tiles_per_split, cache_tiles, tree_tiles, nblocks;
-    int spread;        // every workgroup of a group merges a share of its rows (the grid is resident)
     float scale_log2;
 };
 
@@ -132,17 +127,16 @@ Plan make_plan(int B, int N, int Hq, int Hkv, int L) {
 }
 
 struct WsLayout {
-    size_t counter_off, done_off, part_o_off, part_ml_off, total;
+    size_t counter_off, part_o_off, part_ml_off, total;
 };
 
 WsLayout workspace_layout(int B, int Hkv, const Plan& p) {
-    WsLayout w{0, 0, 0, 0, 0};
+    WsLayout w{0, 0, 0, 0};
     if (p.nsplit <= 1) return w;
     const size_t groups = (size_t)B * Hkv * p.row_tiles;
     const size_t rows = groups * p.nsplit * p.rows;
     w.counter_off = 0;
-    w.done_off = round_up(groups * sizeof(uint32_t), 256);
-    w.part_o_off = w.done_off + round_up(groups * sizeof(uint32_t), 256);
+    w.part_o_off = round_up(groups * sizeof(uint32_t), 256);
     w.part_ml_off = w.part_o_off + round_up(rows * HD * sizeof(float), 256);
     w.total = w.part_ml_off + round_up(rows * 2 * sizeof(float), 256);
     return w;
@@ -238,36 +232,44 @@ __device__ __forceinline__ float halves_sum(float x) {
 // combines them, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s, writes the output
 // and resets the counter for the next call.  `lds` holds at least
 // 2 * nrows * nsplit floats; `s_flag` is a workgroup-shared int outside them.
-// Rows [r_lo, r_hi) of a split group's output (workgroup-relative rows; the
-// group's partials start at pbase): per row, w_s = 2^(m_s - M) / sum_s
-// 2^(m_s - M) l_s and out = sum_s w_s O_s, summed over s in order.
 template <int NT, int ROWS>
-__device__ void merge_rows(const AttnArgs& a, char* lds, size_t pbase, int r_lo, int r_hi, int row0, int b, int g) {
+__device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp, int row0, int nrows, int b,
+                             int g) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have landed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(&a.counter[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = prev == (uint32_t)a.nsplit - 1;
+    }
+    __syncthreads();
+    if (!*s_flag) return;
+
+    // last workgroup of the group: per row, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s
     const int ns = a.nsplit;
-    const int nr = r_hi - r_lo;
-    if (nr <= 0) return;                         // uniform
-    float* wts = reinterpret_cast<float*>(lds);  // [nr][ns] (m_s, then the weight)
-    float* lsv = wts + nr * ns;                  // [nr][ns] l_s
-    for (int e0 = 0; e0 < nr * ns; e0 += 8 * NT) {
+    float* wts = reinterpret_cast<float*>(lds);  // [nrows][ns] (m_s, then the weight)
+    float* lsv = wts + nrows * ns;               // [nrows][ns] l_s
+    const size_t pbase = (size_t)grp * ns * ROWS;
+    for (int e0 = 0; e0 < nrows * ns; e0 += 8 * NT) {
         float mv[8], lv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int e = min(e0 + k * NT + (int)threadIdx.x, nr * ns - 1);
-            const float* ml = a.part_ml + (pbase + (size_t)(e % ns) * ROWS + r_lo + e / ns) * 2;
+            const int e = min(e0 + k * NT + (int)threadIdx.x, nrows * ns - 1);
+            const float* ml = a.part_ml + (pbase + (size_t)(e % ns) * ROWS + e / ns) * 2;
             mv[k] = ld_dev_f(ml);
             lv[k] = ld_dev_f(ml + 1);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int e = e0 + k * NT + (int)threadIdx.x;
-            if (e < nr * ns) {
+            if (e < nrows * ns) {
                 wts[e] = mv[k];
                 lsv[e] = lv[k];
             }
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nr; i += NT) {
+    for (int i = threadIdx.x; i < nrows; i += NT) {
         float M = -INFINITY;
         for (int s = 0; s < ns; ++s) M = fmaxf(M, wts[i * ns + s]);
         float Lsum = 0.f;
@@ -281,7 +283,7 @@ __device__ void merge_rows(const AttnArgs& a, char* lds, size_t pbase, int r_lo,
     }
     __syncthreads();
     // each thread owns output float4s, two at a time, with 16 split loads in flight
-    const int nout = nr * (HD / 4);
+    const int nout = nrows * (HD / 4);
     for (int e0 = threadIdx.x; e0 < nout; e0 += 2 * NT) {
         int ei[2];
         f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -290,7 +292,7 @@ __device__ void merge_rows(const AttnArgs& a, char* lds, size_t pbase, int r_lo,
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 ei[u] = min(e0 + u * NT, nout - 1);
-                const float* src = a.part_o + (pbase + r_lo + ei[u] / (HD / 4)) * HD + 4 * (ei[u] % (HD / 4));
+                const float* src = a.part_o + (pbase + ei[u] / (HD / 4)) * HD + 4 * (ei[u] % (HD / 4));
 #pragma unroll
                 for (int k = 0; k < 8; ++k) v[u][k] = ld_dev_f4(src + (size_t)min(s0 + k, ns - 1) * ROWS * HD);
             }
@@ -305,52 +307,11 @@ __device__ void merge_rows(const AttnArgs& a, char* lds, size_t pbase, int r_lo,
             const int e = e0 + u * NT;
             if (e >= nout) continue;
             const int i = e / (HD / 4), d4 = e % (HD / 4);
-            const int rr = row0 + r_lo + i;
+            const int rr = row0 + i;
             const int nd = rr / a.G, hd = g * a.G + rr % a.G;
             *reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.N + nd) * a.Hq + hd) * HD + 4 * d4) = acc[u];
         }
     }
-}
-
-// Split-KV merge, after this workgroup published its partial.  With a
-// resident grid (a.spread) every workgroup of the group waits until all of the
-// group's partials are published and merges its share of the rows; the last
-// to arrive at the wait returns the two counters to zero.  Otherwise the last
-// workgroup to publish merges every row.
-template <int NT, int ROWS>
-__device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp, int row0, int nrows, int b,
-                             int g, int split) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have landed
-    __syncthreads();
-    const int ns = a.nsplit;
-    const size_t pbase = (size_t)grp * ns * ROWS;
-    if (a.spread) {
-        if (threadIdx.x == 0) {
-            __hip_atomic_fetch_add(&a.counter[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            uint32_t spins = 0;
-            while (__hip_atomic_load(&a.counter[grp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)ns &&
-                   ++spins < kMergeSpinLimit)
-                __builtin_amdgcn_s_sleep(1);
-            // past the wait: the last one here clears both counters for the next call
-            if (__hip_atomic_fetch_add(&a.done[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)ns - 1) {
-                __hip_atomic_store(&a.counter[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&a.done[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();
-        const int per = (nrows + ns - 1) / ns;
-        merge_rows<NT, ROWS>(a, lds, pbase, min(nrows, split * per), min(nrows, split * per + per), row0, b, g);
-        return;
-    }
-    if (threadIdx.x == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(&a.counter[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = prev == (uint32_t)ns - 1;
-    }
-    __syncthreads();
-    if (!*s_flag) return;
-    merge_rows<NT, ROWS>(a, lds, pbase, 0, nrows, row0, b, g);
     if (threadIdx.x == 0)
         __hip_atomic_store(&a.counter[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
 }
@@ -751,7 +712,7 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
     }
 
     // ---- split-KV: the partials are published; the last workgroup merges ----
-    merge_splits<kThreads, ROWS>(a, lds, &s_last, grp, row0, nrows, b, g, split);
+    merge_splits<kThreads, ROWS>(a, lds, &s_last, grp, row0, nrows, b, g);
 }
 
 // fp16 packing for the large-row kernel below
@@ -1111,35 +1072,9 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
             st_dev_f(a.part_ml + prow * 2 + 1, l_tot);
         }
     }
-    merge_splits<64 * NW, ROWS>(a, lds, s_flag, grp, row0, nrows, b, g, split);
+    merge_splits<64 * NW, ROWS>(a, lds, s_flag, grp, row0, nrows, b, g);
 }
 
-}  // namespace
-}  // namespace tv
-
-namespace tv {
-namespace {
-// Workgroups of one attention variant resident at once on the current device
-// (occupancy query, cached per device and variant).
-int resident_capacity(int variant) {
-    static std::mutex mu;
-    static int cache[64][4] = {};
-    int dev = 0;
-    if (variant < 0 || variant > 3 || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    std::lock_guard<std::mutex> lock(mu);
-    if (cache[dev][variant] == 0) {
-        int ncu = 0, per = 0;
-        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) return 0;
-        const void* fn = variant == 0   ? reinterpret_cast<const void*>(tree_attention_kernel<4, 32, 2, 1, 4>)
-                         : variant == 1 ? reinterpret_cast<const void*>(tree_attention_kernel<4, 32, 2, 2, 4>)
-                         : variant == 2 ? reinterpret_cast<const void*>(tree_attention_kernel<2, 64, 2, 2, 4>)
-                                        : reinterpret_cast<const void*>(tree_attention_wide_kernel<5>);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, variant == 3 ? 512 : 256, 0) != hipSuccess || per < 1)
-            return 0;
-        cache[dev][variant] = ncu * per;
-    }
-    return cache[dev][variant];
-}
 }  // namespace
 }  // namespace tv
 
@@ -1181,7 +1116,6 @@ extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, con
     a.out = out;
     char* ws = static_cast<char*>(workspace);
     a.counter = wl.total ? reinterpret_cast<uint32_t*>(ws + wl.counter_off) : nullptr;
-    a.done = wl.total ? reinterpret_cast<uint32_t*>(ws + wl.done_off) : nullptr;
     a.part_o = wl.total ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
     a.part_ml = wl.total ? reinterpret_cast<float*>(ws + wl.part_ml_off) : nullptr;
     a.N = N;
@@ -1199,11 +1133,6 @@ extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, con
     const long nblocks = (long)B * Hkv * p.nsplit * p.row_tiles;
     if (nblocks > 0x7fffffffL) return TV_ERR_UNSUPPORTED;
     a.nblocks = (int)nblocks;
-    // the shared merge waits for every workgroup of a group: only when the
-    // whole grid is resident at once, and only for eight splits or more (with
-    // fewer, the last workgroup's merge is short and the wait costs as much:
-    // 4 splits of 240 rows measured ~1% slower shared)
-    a.spread = p.nsplit >= 8 && nblocks <= resident_capacity(p.variant);
 
     hipStream_t st = (hipStream_t)stream;
     switch (p.variant) {
