@@ -159,7 +159,11 @@ int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t
  * resident workgroup capacity).
  * Execution: one launch sized to the device's resident workgroup capacity;
  * every sequence is walked by a team of workgroups that synchronise through
- * the workspace, so calls that share a workspace must not overlap.
+ * the workspace, so calls that share a workspace must not overlap.  The
+ * teams' waits assume that every workgroup of the launch runs at once (no
+ * other work holds the device's compute units for long).  Each wait is
+ * bounded (about a second); one that runs out lets the call finish, with
+ * undefined outputs for that team's sequences.
  */
 size_t tv_spec_accept_workspace(int B, int N, int V, int greedy);
 int tv_spec_accept(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
