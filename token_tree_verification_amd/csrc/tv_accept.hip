@@ -593,15 +593,23 @@ __device__ __forceinline__ void target_slice(const float* qrow, float Mq, float 
 // the slice total through rounding, or tau < 0 meaning "fallback"), the last
 // element with res[e] > 0.  Returns the slice-local index (or -1 if no mass).
 __device__ __forceinline__ int slice_draw(const float* res, int nsl, double tau, double* wt, int* s_tok) {
-    const int t = threadIdx.x;
+    // an opaque copy of the thread index: what is derived from it stays here
+    // instead of occupying registers across the kernel's sequence loop
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
     const int run = (nsl + kThreads - 1) / kThreads;
     const int a0 = min(nsl, t * run), a1 = min(nsl, a0 + run);
+    // the run's total, read from a rotated start (thread t begins t steps in):
+    // the lanes of a wave then touch different LDS banks at every step instead
+    // of runs `run` words apart (a 32-way conflict for 32-element runs)
     double sum = 0.0;
     int lastp = -1;
-    for (int e = a0; e < a1; ++e) {
-        const float v = res[e];
+    const int len = a1 - a0;
+    for (int i = 0, k = len > 0 ? t % len : 0; i < len; ++i) {
+        const float v = res[a0 + k];
         sum += (double)v;
-        if (v > 0.f) lastp = e;
+        if (v > 0.f) lastp = max(lastp, a0 + k);
+        if (++k == len) k = 0;
     }
     double excl, tot;
     const double incl = block_scan_d(sum, wt, excl, tot);
