@@ -664,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
     __shared__ double s_rejZ[GREEDY ? 1 : TV_MAX_NODES];
     __shared__ int s_rej[GREEDY ? 1 : TV_MAX_NODES];
     __shared__ float s_wx[2], s_nwx[2];
-    __shared__ double s_oexcl;
+    __shared__ double s_oexcl, s_target;
     __shared__ int s_ok, s_tok, s_owner, s_fallback, s_rowctr, s_hitw[kWaves], s_lastw[kWaves];
     __shared__ uint64_t s_base;
 
@@ -900,15 +900,47 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                     mt = em == -INFINITY ? 0.0 : (double)es * (double)__builtin_amdgcn_exp2f((em - s_M[u]) * c);
                 }
             }
-            double mexcl, total;
-            const double mincl = block_scan_d(mt, s_wt, mexcl, total);
-            const double target = ut * total;
             // owner: the first slice whose running mass exceeds the target; else the last with mass
-            {
+            double target;
+            if (W <= kWave) {
+                // every mass sits in wave 0, whose own scan is the block scan's result
+                // (the other waves add exact zeros): one barrier publishes the owner
+                if (tid < kWave) {
+                    int lane = tid;
+                    asm volatile("" : "+v"(lane));  // formed here, not held across the sequence loop
+                    double v = mt;
+#pragma unroll
+                    for (int o = 1; o < kWave; o <<= 1) {
+                        const double y = __shfl_up(v, o);
+                        if (lane >= o) v += y;
+                    }
+                    const double prev = __shfl_up(v, 1);
+                    const double tot = __shfl(v, kWave - 1);
+                    const double tg = ut * tot;
+                    const bool has = tid < W && mt > 0.0;
+                    const uint64_t hit = __ballot(has && v > tg);
+                    const uint64_t pos = __ballot(has);
+                    const int own = hit ? __ffsll((unsigned long long)hit) - 1
+                                        : (pos ? 63 - __clzll((unsigned long long)pos) : -1);
+                    if (tid == 0) {
+                        s_owner = own;
+                        s_fallback = hit == 0;
+                        s_target = tg;
+                    }
+                    if (tid == own) s_oexcl = lane == 0 ? 0.0 : prev;
+                }
+                __syncthreads();
+                target = s_target;
+            } else {
+                double mexcl, total;
+                const double mincl = block_scan_d(mt, s_wt, mexcl, total);
+                target = ut * total;
                 const bool has = tid < W && mt > 0.0;
                 const uint64_t hit = __ballot(has && mincl > target);
                 const uint64_t pos = __ballot(has);
-                const int lane = tid & 63, wv = tid >> 6;
+                int t = tid;
+                asm volatile("" : "+v"(t));  // formed here, not held across the sequence loop
+                const int lane = t & 63, wv = t >> 6;
                 if (lane == 0) {
                     s_hitw[wv] = hit ? wv * kWave + __ffsll((unsigned long long)hit) - 1 : -1;
                     s_lastw[wv] = pos ? wv * kWave + 63 - __clzll((unsigned long long)pos) : -1;
