@@ -227,41 +227,44 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Split-KV merge: every workgroup of a row group has published its partial
-// (max, sum, unnormalised O); the last one to arrive (device-scope counter)
-// combines them, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s, writes the output
-// and resets the counter for the next call.  `lds` holds at least
-// 2 * nrows * nsplit floats; `s_flag` is a workgroup-shared int outside them.
-template <int NT, int ROWS>
-__device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp, int row0, int nrows, int b,
-                             int g) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have landed
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(&a.counter[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = prev == (uint32_t)a.nsplit - 1;
-    }
-    __syncthreads();
-    if (!*s_flag) return;
-
-    // last workgroup of the group: per row, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s
+// The merge itself.  Per row, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s and
+// out = sum_s w_s O_s.  Each thread owns U output float4s at a time (stride
+// NT) and loads SC splits of each per round, U * SC loads in flight.  With
+// HOIST the first round's loads are issued before the (m, l) loads, so that
+// both arrive in one round trip.  `lds` holds at least 2 * nrows * nsplit
+// floats.
+template <int NT, int ROWS, int U, int SC, bool HOIST>
+__device__ void merge_partials(const AttnArgs& a, char* lds, int grp, int row0, int nrows, int b, int g) {
     const int ns = a.nsplit;
     float* wts = reinterpret_cast<float*>(lds);  // [nrows][ns] (m_s, then the weight)
     float* lsv = wts + nrows * ns;               // [nrows][ns] l_s
     const size_t pbase = (size_t)grp * ns * ROWS;
-    for (int e0 = 0; e0 < nrows * ns; e0 += 8 * NT) {
+    const int nout = nrows * (HD / 4);
+    f32x4 v[U][SC];
+    auto load = [&](int e0, int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = min(e0 + u * NT, nout - 1);
+            const float* src = a.part_o + (pbase + e / (HD / 4)) * HD + 4 * (e % (HD / 4));
+#pragma unroll
+            for (int k = 0; k < SC; ++k) v[u][k] = ld_dev_f4(src + (size_t)min(s0 + k, ns - 1) * ROWS * HD);
+        }
+    };
+    int e0 = threadIdx.x, s0 = 0;
+    if (HOIST) load(e0, s0);
+
+    for (int f0 = 0; f0 < nrows * ns; f0 += 8 * NT) {
         float mv[8], lv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int e = min(e0 + k * NT + (int)threadIdx.x, nrows * ns - 1);
+            const int e = min(f0 + k * NT + (int)threadIdx.x, nrows * ns - 1);
             const float* ml = a.part_ml + (pbase + (size_t)(e % ns) * ROWS + e / ns) * 2;
             mv[k] = ld_dev_f(ml);
             lv[k] = ld_dev_f(ml + 1);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int e = e0 + k * NT + (int)threadIdx.x;
+            const int e = f0 + k * NT + (int)threadIdx.x;
             if (e < nrows * ns) {
                 wts[e] = mv[k];
                 lsv[e] = lv[k];
@@ -282,36 +285,66 @@ __device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp,
         for (int s = 0; s < ns; ++s) wts[i * ns + s] *= inv;
     }
     __syncthreads();
-    // each thread owns output float4s, two at a time, with 16 split loads in flight
-    const int nout = nrows * (HD / 4);
-    for (int e0 = threadIdx.x; e0 < nout; e0 += 2 * NT) {
-        int ei[2];
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        for (int s0 = 0; s0 < ns; s0 += 8) {
-            f32x4 v[2][8];
+
+    f32x4 acc[U];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                ei[u] = min(e0 + u * NT, nout - 1);
-                const float* src = a.part_o + (pbase + ei[u] / (HD / 4)) * HD + 4 * (ei[u] % (HD / 4));
+    for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!HOIST && e0 < nout) load(e0, s0);
+    while (e0 < nout) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) v[u][k] = ld_dev_f4(src + (size_t)min(s0 + k, ns - 1) * ROWS * HD);
+        for (int u = 0; u < U; ++u) {
+            const int i = min(e0 + u * NT, nout - 1) / (HD / 4);
+#pragma unroll
+            for (int k = 0; k < SC; ++k)
+                if (s0 + k < ns) acc[u] += wts[i * ns + s0 + k] * v[u][k];
+        }
+        s0 += SC;
+        if (s0 >= ns) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * NT;
+                if (e < nout) {
+                    const int i = e / (HD / 4), d4 = e % (HD / 4);
+                    const int rr = row0 + i;
+                    const int nd = rr / a.G, hd = g * a.G + rr % a.G;
+                    *reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.N + nd) * a.Hq + hd) * HD + 4 * d4) = acc[u];
+                }
+                acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (s0 + k < ns) acc[u] += wts[(ei[u] / (HD / 4)) * ns + s0 + k] * v[u][k];
+            s0 = 0;
+            e0 += U * NT;
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int e = e0 + u * NT;
-            if (e >= nout) continue;
-            const int i = e / (HD / 4), d4 = e % (HD / 4);
-            const int rr = row0 + i;
-            const int nd = rr / a.G, hd = g * a.G + rr % a.G;
-            *reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.N + nd) * a.Hq + hd) * HD + 4 * d4) = acc[u];
-        }
+        if (e0 < nout) load(e0, s0);
     }
+}
+
+// Split-KV merge: every workgroup of a row group has published its partial
+// (max, sum, unnormalised O); the last one to arrive (device-scope counter)
+// combines them, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s, writes the output
+// and resets the counter for the next call.  `lds` holds at least
+// 2 * nrows * nsplit floats; `s_flag` is a workgroup-shared int outside them.
+template <int NT, int ROWS>
+__device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp, int row0, int nrows, int b,
+                             int g) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have landed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(&a.counter[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = prev == (uint32_t)a.nsplit - 1;
+    }
+    __syncthreads();
+    if (!*s_flag) return;
+
+    // last workgroup of the group.  Up to four splits: 32 loads in flight per
+    // thread (16 in the 512-thread kernel, whose register budget is half as
+    // large), the first round issued early.  More splits: 16 loads, issued
+    // once the weights are known (measured faster for eleven splits of 24 rows).
+    constexpr int F = NT >= 512 ? 16 : 32;
+    if (a.nsplit <= 4)
+        merge_partials<NT, ROWS, F / 4, 4, true>(a, lds, grp, row0, nrows, b, g);
+    else
+        merge_partials<NT, ROWS, 2, 8, false>(a, lds, grp, row0, nrows, b, g);
     if (threadIdx.x == 0)
         __hip_atomic_store(&a.counter[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
 }
