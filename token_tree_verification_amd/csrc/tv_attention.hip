@@ -150,19 +150,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-__device__ __forceinline__ void st_dev_f4(float* p, f32x4 v) {
-    uint64_t* q = reinterpret_cast<uint64_t*>(p);
-    __hip_atomic_store(q, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Split partials cross workgroups (and XCDs, whose L2s are not coherent with
+// each other) through 16-byte buffer accesses with the cache policy of an
+// agent-scope atomic access (sc1): one instruction per float4 where two 8-byte
+// atomics would be needed.  A resource covers one range of under 4 GiB.
+constexpr int kDevCoherent = 1 << 4;  // cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ f32x4 ld_dev_f4(const float* p) {
-    uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
-    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
-                 __uint_as_float((uint32_t)(b >> 32))};
+__device__ __forceinline__ void st_dev_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDevCoherent);
+}
+__device__ __forceinline__ f32x4 ld_dev_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDevCoherent));
 }
 __device__ __forceinline__ void st_dev_f(float* p, float v) {
     __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -241,13 +241,14 @@ __device__ void merge_partials(const AttnArgs& a, char* lds, int grp, int row0, 
     const size_t pbase = (size_t)grp * ns * ROWS;
     const int nout = nrows * (HD / 4);
     f32x4 v[U][SC];
+    const __amdgpu_buffer_rsrc_t po = dev_rsrc(a.part_o + pbase * HD, (uint32_t)(ns * ROWS * HD * 4));
     auto load = [&](int e0, int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = min(e0 + u * NT, nout - 1);
-            const float* src = a.part_o + (pbase + e / (HD / 4)) * HD + 4 * (e % (HD / 4));
+            const uint32_t off = (uint32_t)(((e / (HD / 4)) * HD + 4 * (e % (HD / 4))) * 4);
 #pragma unroll
-            for (int k = 0; k < SC; ++k) v[u][k] = ld_dev_f4(src + (size_t)min(s0 + k, ns - 1) * ROWS * HD);
+            for (int k = 0; k < SC; ++k) v[u][k] = ld_dev_b128(po, off + (uint32_t)(min(s0 + k, ns - 1) * ROWS * HD * 4));
         }
     };
     int e0 = threadIdx.x, s0 = 0;
@@ -338,13 +339,14 @@ __device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp,
 
     // last workgroup of the group.  Up to four splits: 32 loads in flight per
     // thread (16 in the 512-thread kernel, whose register budget is half as
-    // large), the first round issued early.  More splits: 16 loads, issued
-    // once the weights are known (measured faster for eleven splits of 24 rows).
+    // large), the first round issued early.  More splits: chunks of twelve
+    // splits for four (two) outputs, 48 (24) loads issued once the weights are
+    // known (eleven splits of 24 rows: one round, no issue-early gain).
     constexpr int F = NT >= 512 ? 16 : 32;
     if (a.nsplit <= 4)
         merge_partials<NT, ROWS, F / 4, 4, true>(a, lds, grp, row0, nrows, b, g);
     else
-        merge_partials<NT, ROWS, 2, 8, false>(a, lds, grp, row0, nrows, b, g);
+        merge_partials<NT, ROWS, F / 8, 12, false>(a, lds, grp, row0, nrows, b, g);
     if (threadIdx.x == 0)
         __hip_atomic_store(&a.counter[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
 }
@@ -664,18 +666,20 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
             }
             return;
         }
+        const __amdgpu_buffer_rsrc_t pw =
+            dev_rsrc(a.part_o + ((size_t)grp * a.nsplit + split) * ROWS * HD, (uint32_t)(ROWS * HD * 4));
 #pragma unroll
         for (int j = 0; j < RBW; ++j) {
             if (!row_ok[j]) continue;
             const size_t prow = ((size_t)grp * a.nsplit + split) * ROWS + (row[j] - row0);
-            float* dst = a.part_o + prow * HD;
+            const uint32_t ob = (uint32_t)((row[j] - row0) * HD * 4);
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    st_dev_f4(dst + 32 * blk + 8 * q + 4 * hf,
-                              f32x4{o_acc[j][blk][4 * q], o_acc[j][blk][4 * q + 1], o_acc[j][blk][4 * q + 2],
-                                    o_acc[j][blk][4 * q + 3]});
+                    st_dev_b128(pw, ob + (uint32_t)((32 * blk + 8 * q + 4 * hf) * 4),
+                                f32x4{o_acc[j][blk][4 * q], o_acc[j][blk][4 * q + 1], o_acc[j][blk][4 * q + 2],
+                                      o_acc[j][blk][4 * q + 3]});
             if (hf == 0) {
                 st_dev_f(a.part_ml + prow * 2, m_log[j]);
                 st_dev_f(a.part_ml + prow * 2 + 1, l_tot[j]);
@@ -734,7 +738,9 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
                     *reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.N + node) * a.Hq + head) * HD + d_lo + 4 * d4) =
                         acc * inv;
                 else
-                    st_dev_f4(a.part_o + prow * HD + d_lo + 4 * d4, acc);
+                    st_dev_b128(dev_rsrc(a.part_o + ((size_t)grp * a.nsplit + split) * ROWS * HD,
+                                         (uint32_t)(ROWS * HD * 4)),
+                                (uint32_t)((rr * HD + d_lo + 4 * d4) * 4), acc);
             }
             if (a.nsplit > 1 && wave % KG == 0) {
                 st_dev_f(a.part_ml + prow * 2, M);
@@ -1093,13 +1099,15 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     }
     if (row_ok) {
         const size_t prow = ((size_t)grp * a.nsplit + split) * ROWS + (row - row0);
-        float* dst = a.part_o + prow * HD;
+        const __amdgpu_buffer_rsrc_t pw =
+            dev_rsrc(a.part_o + ((size_t)grp * a.nsplit + split) * ROWS * HD, (uint32_t)(ROWS * HD * 4));
+        const uint32_t ob = (uint32_t)((row - row0) * HD * 4);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                st_dev_f4(dst + 32 * blk + 8 * q + 4 * hf,
-                          f32x4{o_acc[blk][4 * q], o_acc[blk][4 * q + 1], o_acc[blk][4 * q + 2], o_acc[blk][4 * q + 3]});
+                st_dev_b128(pw, ob + (uint32_t)((32 * blk + 8 * q + 4 * hf) * 4),
+                            f32x4{o_acc[blk][4 * q], o_acc[blk][4 * q + 1], o_acc[blk][4 * q + 2], o_acc[blk][4 * q + 3]});
         if (hf == 0) {
             st_dev_f(a.part_ml + prow * 2, m_log);
             st_dev_f(a.part_ml + prow * 2 + 1, l_tot);
