@@ -109,7 +109,8 @@ def test_attention_tiny_full_compare(tv, w):
 
 
 # shapes hitting each row packing (R = G*N <= 32, <= 64, <= 128, > 128), ragged
-# key tails, single-key caches, empty caches, several row tiles and splits
+# key tails, single-key caches, empty caches, several row tiles and splits,
+# split merges in one round and in several
 @pytest.mark.parametrize("B,N,Hq,Hkv,L,tree", [
     (1, 1, 1, 1, 1, "chain"),
     (2, 1, 8, 8, 0, "chain"),
@@ -125,6 +126,8 @@ def test_attention_tiny_full_compare(tv, w):
     (2, 33, 8, 2, 700, "random"),
     (1, 64, 16, 2, 3000, "random"),
     (1, 17, 16, 1, 128, "chain"),
+    (1, 6, 4, 1, 16384, "chain"),  # 26 splits of 24 rows: merge rounds of 12, 12 and 2
+    (1, 64, 4, 1, 8192, "random"),  # 256 rows, 5 splits: the wide kernel's many-split merge
 ])
 def test_attention_shapes(tv, B, N, Hq, Hkv, L, tree):
     w = Workload("shape", B=B, N=N, Hq=Hq, Hkv=Hkv, D=128, L=L, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),
