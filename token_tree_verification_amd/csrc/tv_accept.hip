@@ -59,6 +59,7 @@ constexpr int kThreads = 1024;       // one workgroup per CU: no co-resident wor
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxTeamSize = 256;
 constexpr int kMaxTeams = 1024;
+constexpr long kMinMemberBytes = 88 * 1024;  // sampling: logit bytes streamed per member and sequence, at least
 constexpr int kMinSlice = 1024;      // logits per member and row, at least
 constexpr int kMaxSlice = 32768;     // sampling: a member's residual slice lives in LDS (128 KB)
 constexpr int kMaxSpans = 4095;      // greedy: spans of 256 logits per slice, at most
@@ -1039,6 +1040,15 @@ int make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
     if (cap <= 0) return TV_ERR_HIP;
     int wmax = (V + kMinSlice - 1) / kMinSlice;
     if (wmax > kMaxTeamSize) wmax = kMaxTeamSize;
+    // sampling: a small stream (few rows) spread over many members costs more
+    // in merge and exchange round trips than their shares save (a 6-node chain
+    // over 128256 tokens: 62 members took 6% less time than 126, which also
+    // leaves the team on the merge for at most 64 members).  Greedy merges
+    // only (max, argmax) and was slower with the same floor.
+    if (!greedy) {
+        const long wbytes = (2L * N - 1) * (long)V * 4 / kMinMemberBytes;
+        if (wbytes < wmax) wmax = wbytes < 1 ? 1 : (int)wbytes;
+    }
     // sampling keeps a member's residual slice in LDS
     const int wmin = greedy ? (V + kMaxSpans * kSpan - 1) / (kMaxSpans * kSpan) : (V + kMaxSlice - 1) / kMaxSlice;
     if (wmin > kMaxTeamSize) return TV_ERR_UNSUPPORTED;
