@@ -3,10 +3,12 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 tree mask -> ancestor-masked tree attention -> accept/reject walk.  The
-headline workload is "batch 1 linear chain K=5, GQA 32/8 x 128, KV 4096,
-vocab 128256" with temperature-1.0 sampling; the greedy step is reported
-beside it.  Inputs are resident in HBM before timing starts and rotate over
-enough copies to exceed the 256 MB Infinity Cache.
+headline workload is the largest of the five benchmark workloads that fits
+one GPU: "batch 64 dynamic 64-node trees, GQA 64/8 x 128, KV 8192, vocab
+128256" with temperature-1.0 sampling; the greedy step is reported beside it,
+and the other four workloads are measured in the same run under "configs".
+Inputs are resident in HBM before timing starts and rotate over enough copies
+to exceed the 256 MB Infinity Cache.
 
 Prints ONE JSON line (rank 0) with the throughput (verified tree-nodes/s),
 the roofline of the dominant call measured live with HIP events on its
@@ -43,7 +45,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="headline workload (default: the largest one, c4)")
+    ap.add_argument("--also", default="c1,c2,c3,c5",
+                    help="other workloads measured in the same run and reported under 'configs'")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload alone")
     ap.add_argument("--temperature", type=float, default=None, help="sampling temperature (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
@@ -233,72 +239,96 @@ def kernel_sources_digest(files):
     return h.hexdigest()
 
 
-def counted_traffic(workload, kernel_key, files):
-    """HBM bytes per launch of ``kernel_key`` on ``workload`` from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+def _profile_record(path, kernel_key, files):
+    """The JSON record of ``kernel_key`` in a committed rocprofv3 summary under
+    profiles/, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", path)
     if not os.path.exists(path):
         return None
-    text = open(path).read()
-    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
     if not m:
         return None
     rec = json.loads(m.group(1)).get("kernels", {}).get(kernel_key)
     if not rec or rec.get("sources_sha256") != kernel_sources_digest(files):
         return None
-    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+    return rec
+
+
+def counted_traffic(workload, kernel_key, files):
+    """HBM bytes per launch of ``kernel_key`` on ``workload`` (FETCH_SIZE plus
+    WRITE_SIZE, calibrated on a plain copy) from the committed summary."""
+    rec = _profile_record(f"traffic_{workload}.md", kernel_key, files)
+    return None if rec is None else int(rec["fetch_bytes"]) + int(rec["write_bytes"])
+
+
+def counted_mfma(workload, files):
+    """MFMA counters of the attention kernel on ``workload`` from the committed
+    summary: busy fraction of the matrix pipes and the MFMA FLOPs issued."""
+    rec = _profile_record(f"mfma_{workload}.md", "tree_attention_kernel", files)
+    if rec is None:
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac", "mfma_flops_issued", "mfma_flops_per_alg_flop") if k in rec}
 
 
 def cpu_baseline(w, inputs, temperature, seconds):
-    """The oracle (numpy fp64 attention + C walk) on the host cores, on a bounded
-    sample: whole verification steps of this workload, repeated until about
-    ``seconds`` of CPU time has been spent (at least one step)."""
+    """The oracle as it stands (numpy fp64 attention, C walk) on the host
+    cores, on a bounded sample of the workload: whole sequences (every head of
+    the attention, then the sampling walk), one after another, until about
+    ``seconds`` have been spent (at least one).  Attention and walk are timed
+    separately.  numpy's BLAS pool is set explicitly to the host's CPU share
+    (OMP_NUM_THREADS when the environment fixes it, else os.cpu_count())."""
     import numpy as np
     import oracle
     from workloads import bf16_to_f64
     Q, Kc, Vc, Kt, Vt, q, p, draft, parent = inputs
-    host = [bf16_to_f64(t) for t in (Q, Kc, Vc, Kt, Vt)]
-    qn, pn, dn, parn = (t.cpu().numpy() for t in (q, p, draft, parent))
+    host_cpus = os.cpu_count() or 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", host_cpus) or host_cpus)
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads, user_api="blas")
     except Exception:
-        threads = os.cpu_count() or 1
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.tree_mask(parn)
-        oracle.tree_attention(*host, parn)
-        oracle.spec_accept(qn, pn, dn, parn, seed=0, temperature=temperature)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(steps * w.B * (w.N - 1) / el, 3), "unit": "tree-nodes/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{steps} full verification step(s) of the benchmark workload (mask + fp64 attention + "
-                      f"sampling walk at T={temperature}) in {el:.1f} s"}
+        pass
+    try:
+        parn = parent.cpu().numpy()
+        t_attn = t_acc = 0.0
+        seqs = 0
+        while seqs < w.B:
+            b = seqs
+            host = [bf16_to_f64(t[b:b + 1]) for t in (Q, Kc, Vc, Kt, Vt)]
+            t0 = time.perf_counter()
+            oracle.tree_mask(parn[b:b + 1])
+            oracle.tree_attention(*host, parn[b:b + 1])
+            t1 = time.perf_counter()
+            qn, pn, dn = (t[b:b + 1].cpu().numpy() for t in (q, p, draft))
+            t2 = time.perf_counter()
+            oracle.spec_accept(qn, pn, dn, parn[b:b + 1], seed=0, temperature=temperature)
+            t3 = time.perf_counter()
+            t_attn += t1 - t0
+            t_acc += t3 - t2
+            seqs += 1
+            if t_attn + t_acc >= seconds:
+                break
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    nodes = seqs * (w.N - 1)
+    return {"value": round(nodes / (t_attn + t_acc), 3), "unit": "tree-nodes/s", "cores": threads,
+            "kind": "oracle", "host_cpus": host_cpus, "blas_threads": threads,
+            "attention_s": round(t_attn, 3), "accept_s": round(t_acc, 3),
+            "sample": f"{seqs} of the workload's {w.B} sequence(s): mask + fp64 attention over every head + "
+                      f"sampling walk at T={temperature}, {t_attn:.1f} s attention and {t_acc:.1f} s walk"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (verification of independent "
-              f"sequences shards by batch with no communication).", file=sys.stderr)
-        return 2
-    import numpy as np
-    import torch
-
-    import token_tree_verification_amd as tv
+def measure(name, args, tv, torch, dev, stream, lead_of, headline):
+    """Time one workload: whole sampling and greedy steps, then each call on
+    its own.  Returns the result record and (headline only) the first input
+    copy for the CPU baseline."""
     from workloads import CONFIGS, CONFIG_TEXT, accept_inputs, attention_inputs
 
-    w = CONFIGS[args.config]
+    w = CONFIGS[name]
     temps = [t for t in w.temperatures if t > 0]
-    T = args.temperature if args.temperature is not None else (temps[0] if temps else 1.0)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.Stream(dev)  # every call of the step is issued (and captured) here
-    torch.cuda.set_stream(stream)
-
+    T = args.temperature if (args.temperature is not None and headline) else (temps[0] if temps else 1.0)
     parents = w.parents()
     per_copy = attention_bytes(w) + accept_bytes(w, False)
     ncopies = max(1, min(16, math.ceil(1.5 * MALL_BYTES / per_copy)))
@@ -306,14 +336,13 @@ def main():
     for c in range(ncopies):
         Q, Kc, Vc, Kt, Vt = attention_inputs(w, device=dev, seed=w.data_seed + 100 * c)
         q, p, draft, parent = accept_inputs(w, device=dev, seed=w.data_seed + 100 * c, parent=parents)
-        if c == 0:
+        if c == 0 and headline:
             first_inputs = (Q, Kc, Vc, Kt, Vt, q, p, draft, parent)
         copies.append(dict(
             sample=Step(tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, False, T, w.philox_seed, dev, stream),
             greedy=Step(tv, w, Q, Kc, Vc, Kt, Vt, q, p, draft, parent, True, 1.0, w.philox_seed, dev, stream)))
     torch.cuda.synchronize()
 
-    # warmup (eager), then record one graph per input copy and mode
     for s in range(args.warmup):
         copies[s % ncopies]["sample"].run()
         copies[s % ncopies]["greedy"].run()
@@ -334,26 +363,20 @@ def main():
             return lambda s: copies[s % ncopies][mode].graph.replay()
         return lambda s: copies[s % ncopies][mode].run()
 
-    copy_calibration(torch, dev)
-    cyc_ms = sleep_cycles_per_ms(torch, stream)
-    # enough lead for the host to queue every call of the timed loop
-    lead = lambda calls: cyc_ms * max(2.0, 0.05 * calls)
-
-    # timed: whole steps, sampling mode (headline)
-    ms_step = time_batch(full("sample"), args.steps, stream, torch, lead(3 * args.steps))
-    ms_greedy = time_batch(full("greedy"), args.steps, stream, torch, lead(3 * args.steps))
+    # timed: whole steps, sampling mode (headline) and greedy mode
+    ms_step = time_batch(full("sample"), args.steps, stream, torch, lead_of(3 * args.steps))
+    ms_greedy = time_batch(full("greedy"), args.steps, stream, torch, lead_of(3 * args.steps))
     # per-call durations: `steps` launches of one call back to back (rotating
     # over the input copies) between two events on the launch stream
     calls = {"mask": lambda s: copies[s % ncopies]["sample"].mask(),
              "attention": lambda s: copies[s % ncopies]["sample"].attention(),
              "accept": lambda s: copies[s % ncopies]["sample"].accept(),
              "accept_greedy": lambda s: copies[s % ncopies]["greedy"].accept()}
-    per_all = {n: time_batch(fn, args.steps, stream, torch, lead(args.steps)) for n, fn in calls.items()}
-    per = {k: per_all[k] for k in ("mask", "attention", "accept")}
-    per_g = {"accept_greedy": per_all["accept_greedy"]}
+    per = {n: time_batch(fn, args.steps, stream, torch, lead_of(args.steps)) for n, fn in calls.items()}
+    del copies
+    torch.cuda.synchronize()
 
     nodes = w.B * (w.N - 1)
-    value = nodes / (ms_step / 1e3)
     a_bytes = attention_bytes(w)
     a_flops = attention_flops(w, parents)
     c_bytes = accept_bytes(w, False)
@@ -370,51 +393,109 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
-        roof["kernel"] = "tv::tree_attention_kernel (tv_tree_attention, one launch)"
+        roof["kernel"] = "tv_tree_attention (one launch of tv::tree_attention_kernel / tree_attention_wide_kernel)"
         roof["algorithmic_bytes"] = a_bytes
         roof["algorithmic_flops"] = a_flops
         roof["avg_us"] = round(per["attention"] * 1e3, 3)
         roof["traffic"] = counted_traffic(w.name, "tree_attention_kernel", ATTN_SOURCES)
+        mf = counted_mfma(w.name, ATTN_SOURCES)
+        if mf is not None:
+            roof["mfma_counters"] = mf
     else:
         roof = {"bound": "hbm", "achieved": round(acc_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(acc_gbs / HBM_PEAK_GBS, 4),
                 "kernel": "tv::spec_accept_kernel<false, true> (tv_spec_accept sampling, one launch)",
                 "algorithmic_bytes": c_bytes, "avg_us": round(per["accept"] * 1e3, 3)}
         roof["traffic"] = counted_traffic(w.name, "spec_accept_kernel<false, true>", ACC_SOURCES)
+    rec = {
+        "workload": f"{w.name}: {CONFIG_TEXT[w.name]}",
+        "value": round(nodes / (ms_step / 1e3), 1),
+        "ms_per_step": round(ms_step, 5),
+        "config": {"workload": f"{w.name}: {CONFIG_TEXT[w.name]}", "batch": w.B, "tree_nodes": w.N,
+                   "draft_nodes": w.N - 1, "heads_q_kv": [w.Hq, w.Hkv], "head_dim": w.D, "kv_len": w.L,
+                   "vocab": w.V, "mode": f"sampling T={T}", "input_copies": ncopies,
+                   "launch": "hip-graph replay" if use_graph else "back-to-back launches on one stream"},
+        "roofline": roof,
+        "calls_us": {k: round(v * 1e3, 3) for k, v in per.items()},
+        "attention": {"GB/s": round(attn_gbs, 1), "TFLOP/s": round(attn_tflops, 3),
+                      "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "bound": "mfma" if mfma_bound else "hbm"},
+        "accept": {"GB/s": round(acc_gbs, 1), "hbm_frac": round(acc_gbs / HBM_PEAK_GBS, 4),
+                   "greedy_GB/s": round(accept_bytes(w, True) / (per["accept_greedy"] / 1e3) / 1e9, 1),
+                   "greedy_hbm_frac": round(accept_bytes(w, True) / (per["accept_greedy"] / 1e3) / 1e9
+                                            / HBM_PEAK_GBS, 4)},
+        "greedy": {"value": round(nodes / (ms_greedy / 1e3), 1), "ms_per_step": round(ms_greedy, 5)},
+        "temperature": T,
+    }
+    return rec, first_inputs
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (verification of independent "
+              f"sequences shards by batch with no communication).", file=sys.stderr)
+        return 2
+    import torch
+
+    import token_tree_verification_amd as tv
+    from workloads import CONFIGS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)  # every call of the step is issued (and captured) here
+    torch.cuda.set_stream(stream)
+
+    copy_calibration(torch, dev)
+    cyc_ms = sleep_cycles_per_ms(torch, stream)
+    # enough lead for the host to queue every call of the timed loop
+    lead = lambda calls: cyc_ms * max(2.0, 0.05 * calls)
+
+    head, first_inputs = measure(args.config, args, tv, torch, dev, stream, lead, True)
+    print(f"[bench] {args.config}: {head['ms_per_step'] * 1e3:.1f} us/step, calls_us {head['calls_us']}",
+          file=sys.stderr, flush=True)
+    others = {}
+    if not args.only:
+        for name in [c.strip() for c in args.also.split(",") if c.strip()]:
+            if name == args.config or name not in CONFIGS:
+                continue
+            rec, _ = measure(name, args, tv, torch, dev, stream, lead, False)
+            rec.pop("config", None)
+            others[name] = rec
+            print(f"[bench] {name}: {rec['ms_per_step'] * 1e3:.1f} us/step, calls_us {rec['calls_us']}",
+                  file=sys.stderr, flush=True)
+
+    roof = head["roofline"]
     peaks = achievable_peaks(torch, dev, stream)
     reach = peaks["mfma_loop_bf16_TFLOP/s"] if roof["unit"] == "TFLOP/s" else peaks["hbm_read_GB/s"]
     roof["frac_of_achievable"] = round(roof["achieved"] / reach, 4)
 
     res = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": head["value"],
         "unit": "tree-nodes/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {CONFIG_TEXT[w.name]}", "batch": w.B, "tree_nodes": w.N,
-                   "draft_nodes": w.N - 1, "heads_q_kv": [w.Hq, w.Hkv], "head_dim": w.D, "kv_len": w.L,
-                   "vocab": w.V, "mode": f"sampling T={T}", "input_copies": ncopies,
-                   "launch": "hip-graph replay" if use_graph else "back-to-back launches on one stream"},
+        "config": head["config"],
         "roofline": roof,
-        "calls_us": {k: round(v * 1e3, 3) for k, v in {**per, **per_g}.items()},
-        "attention": {"GB/s": round(attn_gbs, 1), "TFLOP/s": round(attn_tflops, 3),
-                      "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                      "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
-        "accept": {"GB/s": round(acc_gbs, 1), "hbm_frac": round(acc_gbs / HBM_PEAK_GBS, 4),
-                   "greedy_GB/s": round(accept_bytes(w, True) / (per_g["accept_greedy"] / 1e3) / 1e9, 1)},
-        "greedy": {"value": round(nodes / (ms_greedy / 1e3), 1), "ms_per_step": round(ms_greedy, 5)},
+        "calls_us": head["calls_us"],
+        "attention": head["attention"],
+        "accept": head["accept"],
+        "greedy": head["greedy"],
         "achievable": peaks,
+        "configs": others,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, first_inputs, T, args.cpu_seconds)
+        w = CONFIGS[args.config]
+        res["cpu_baseline"] = cpu_baseline(w, first_inputs, head["temperature"], args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
 

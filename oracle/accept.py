@@ -43,6 +43,10 @@ def _load():
         lib.orc_spec_accept.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
                                         ctypes.c_double, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         lib.orc_spec_accept.restype = ctypes.c_int
+        lib.orc_spec_accept_ex.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                           ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                           P, P, P, P, P]
+        lib.orc_spec_accept_ex.restype = ctypes.c_int
         lib.orc_lossless_trials.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_uint64,
                                             ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, P, P]
         lib.orc_lossless_trials.restype = ctypes.c_int
@@ -75,26 +79,33 @@ def uniforms(seed: int, triples) -> np.ndarray:
     return out
 
 
-def spec_accept(q_logits, p_logits, draft, parent, seed=0, temperature=1.0, greedy=False, variant=0):
+def spec_accept(q_logits, p_logits, draft, parent, seed=0, temperature=1.0, greedy=False, variant=0,
+                seq_nodes=None, wor=False, seq_offset=0):
     """Accept/reject walk for every sequence.
 
     q_logits, p_logits: float32 [B,N,V] (p may be None when greedy); draft,
-    parent: int32 [B,N].  Returns dict(accept_len [B], accepted_nodes [B,N],
-    out_tokens [B,N], flags [B], margin [B]).
+    parent: int32 [B,N].  seq_nodes: optional int [B], nodes of each sequence
+    (the others are padding).  wor: siblings drawn without replacement from
+    the draft row of their parent (p row u belongs to node u's children).
+    seq_offset: Philox sequence counter of batch entry 0.  Returns
+    dict(accept_len [B], accepted_nodes [B,N], out_tokens [B,N], flags [B],
+    margin [B]).
     """
     q = np.ascontiguousarray(q_logits, dtype=np.float32)
     B, N, V = q.shape
     p = None if p_logits is None else np.ascontiguousarray(p_logits, dtype=np.float32)
     d = np.ascontiguousarray(draft, dtype=np.int32)
     par = np.ascontiguousarray(parent, dtype=np.int32)
+    sn = None if seq_nodes is None else np.ascontiguousarray(seq_nodes, dtype=np.int32)
     acc_len = np.zeros(B, np.int32)
     acc_nodes = np.zeros((B, N), np.int32)
     toks = np.zeros((B, N), np.int32)
     flags = np.zeros(B, np.int32)
     margin = np.zeros(B, np.float64)
-    rc = _load().orc_spec_accept(_ptr(q), _ptr(p), _ptr(d), _ptr(par), B, N, V, int(seed), float(temperature),
-                                 int(bool(greedy)), int(variant), _ptr(acc_len), _ptr(acc_nodes), _ptr(toks),
-                                 _ptr(flags), _ptr(margin))
+    rc = _load().orc_spec_accept_ex(_ptr(q), _ptr(p), _ptr(d), _ptr(par), _ptr(sn), B, N, V, int(seed),
+                                    float(temperature), int(bool(greedy)), int(variant), int(bool(wor)),
+                                    int(seq_offset) & 0xFFFFFFFF, _ptr(acc_len), _ptr(acc_nodes), _ptr(toks),
+                                    _ptr(flags), _ptr(margin))
     if rc != 0:
         raise ValueError(f"oracle spec_accept rejected its input (status {rc})")
     return dict(accept_len=acc_len, accepted_nodes=acc_nodes, out_tokens=toks, flags=flags, margin=margin)
@@ -102,7 +113,10 @@ def spec_accept(q_logits, p_logits, draft, parent, seed=0, temperature=1.0, gree
 
 def lossless_trials(q_logits, p_logits, parent, temperature, seed0, ntrials, variant=0, draft_mode=0):
     """Run the walk for ``ntrials`` consecutive Philox seeds on one sequence with
-    freshly drawn drafts (draft_mode 0: x_c ~ P_p(c); 1: argmax p_c)."""
+    freshly drawn drafts (draft_mode 0: x_c ~ P_p(c); 1: argmax p_c; 2: the
+    children of u drawn from P_p(u) without replacement, walked in that mode;
+    3: drawn from P_p(u) with replacement, walked in the without-replacement
+    mode)."""
     q = np.ascontiguousarray(q_logits, dtype=np.float32)
     N, V = q.shape
     p = np.ascontiguousarray(p_logits, dtype=np.float32)

@@ -21,12 +21,16 @@ import numpy as np
 from .tree import ancestor_sets
 
 
-def tree_attention(Q, K_cache, V_cache, K_tree, V_tree, parent, scale=None, heads=None):
+def tree_attention(Q, K_cache, V_cache, K_tree, V_tree, parent, scale=None, heads=None, seq_nodes=None,
+                   seq_len=None):
     """All tensors float64 numpy arrays.
 
     Q [B,N,Hq,D]; K_cache, V_cache [B,Hkv,L,D]; K_tree, V_tree [B,N,Hkv,D];
     parent [B,N].  Returns out [B,N,Hq,D] float64.  ``heads`` optionally
     restricts the work to a list of (b, h) pairs (other entries stay NaN).
+    Ragged batches: ``seq_nodes[b]`` nodes and ``seq_len[b]`` committed cache
+    entries of sequence b are real (the rest is padding, never read; outputs
+    of padding nodes stay NaN).
     """
     Q = np.asarray(Q, dtype=np.float64)
     B, N, Hq, D = Q.shape
@@ -39,21 +43,25 @@ def tree_attention(Q, K_cache, V_cache, K_tree, V_tree, parent, scale=None, head
     visible_cache = {}
     for b, h in pairs:
         g = h // G
+        n = N if seq_nodes is None else int(seq_nodes[b])
+        lb = L if seq_len is None else int(seq_len[b])
         if b not in visible_cache:
-            anc = ancestor_sets(parent[b])
-            vis = np.zeros((N, L + N), dtype=bool)
-            vis[:, :L] = True
-            for i in range(N):
+            anc = ancestor_sets(parent[b, :n])
+            vis = np.zeros((n, lb + n), dtype=bool)
+            vis[:, :lb] = True
+            for i in range(n):
                 for j in anc[i]:
-                    vis[i, L + j] = True
+                    vis[i, lb + j] = True
             visible_cache[b] = vis
         vis = visible_cache[b]
-        keys = np.concatenate([np.asarray(K_cache[b, g], np.float64), np.asarray(K_tree[b, :, g], np.float64)], 0)
-        vals = np.concatenate([np.asarray(V_cache[b, g], np.float64), np.asarray(V_tree[b, :, g], np.float64)], 0)
-        s = scale * (Q[b, :, h, :] @ keys.T)
+        keys = np.concatenate([np.asarray(K_cache[b, g, :lb], np.float64),
+                               np.asarray(K_tree[b, :n, g], np.float64)], 0)
+        vals = np.concatenate([np.asarray(V_cache[b, g, :lb], np.float64),
+                               np.asarray(V_tree[b, :n, g], np.float64)], 0)
+        s = scale * (Q[b, :n, h, :] @ keys.T)
         s = np.where(vis, s, -np.inf)
         s = s - s.max(axis=1, keepdims=True)
         e = np.exp(s)
         P = e / e.sum(axis=1, keepdims=True)
-        out[b, :, h, :] = P @ vals
+        out[b, :n, h, :] = P @ vals
     return out

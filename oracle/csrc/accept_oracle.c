@@ -43,6 +43,17 @@
  *    (node, sequence, purpose, 0); U = (first output word >> 8) * 2^-24.
  *    Purpose 0 = accept test, 1 = final sample, 2 = draft sampling in the
  *    lossless harness.
+ *  - Siblings drawn without replacement (EAGLE explainer, static-tree
+ *    verification: the children of a node are several candidates for the
+ *    same next position, taken from the draft's distribution at that node;
+ *    survey explainer, classification table: token-tree verification stays
+ *    lossless).  In this mode p row u is the draft distribution AT node u,
+ *    shared by all of u's children, and child k of u was drawn from it with
+ *    the tokens of children 1..k-1 removed and the rest renormalised.  The
+ *    walk tests child k against exactly that distribution, P^(k), and on
+ *    rejection updates R <- norm(max(0, R - P^(k))).
+ *  - Ragged batches: sequence b uses only its first seq_nodes[b] nodes; the
+ *    arrays keep the batch-wide stride N and the outputs are -1 padded.
  */
 #include <math.h>
 #include <stdint.h>
@@ -166,27 +177,48 @@ static int sample_inverse_cdf(const double* R, int V, double u, int* flags, doub
 }
 
 /* variant: 0 = the rule; 1 = planted mistake for negative controls (siblings
- * are tested against the un-updated target of their parent). */
+ * are tested against the un-updated target of their parent); 2 = planted
+ * mistake for siblings drawn without replacement (each is tested against the
+ * shared row P_p(u) itself instead of P^(k)). */
 typedef struct {
     double* R;   /* current target at the node being expanded */
     double* R0;  /* un-updated target (variant 1 only) */
     double* Pc;  /* draft distribution of the child being tested */
+    double* Pu;  /* without replacement: the shared draft row of the node */
+    int32_t* drawn; /* without replacement: tokens of the node's rejected children */
 } orc_scratch;
 
+/* P^(k): Pu with the tokens drawn[0..nd-1] removed, renormalised.  If no mass
+ * remains the result is all zero. */
+static void without_replacement(const double* Pu, const int32_t* drawn, int nd, int V, double* out) {
+    memcpy(out, Pu, sizeof(double) * (size_t)V);
+    for (int j = 0; j < nd; ++j) out[drawn[j]] = 0.0;
+    double s = 0.0;
+    for (int v = 0; v < V; ++v) s += out[v];
+    for (int v = 0; v < V; ++v) out[v] = (s > 0.0) ? out[v] / s : 0.0;
+}
+
 static int walk_sampling(const float* q, const float* p, const int32_t* draft, const int32_t* parent,
-                         int N, int V, uint64_t seed, uint32_t seq, double T, int variant,
+                         int N, int V, uint64_t seed, uint32_t seq, double T, int variant, int wor,
                          orc_scratch* w, int32_t* acc_nodes, int32_t* tokens, int* flags,
                          double* margin) {
     int u = 0, len = 0;
+    int32_t* drawn = w->drawn;
     for (;;) {
         softmax_T(q + (size_t)u * V, V, T, w->R); /* R = P_q(u) */
         if (variant == 1) memcpy(w->R0, w->R, sizeof(double) * (size_t)V);
-        int has_child = 0, accepted = -1;
+        if (wor) softmax_T(p + (size_t)u * V, V, T, w->Pu); /* the node's draft row */
+        int has_child = 0, accepted = -1, nd = 0;
         for (int c = u + 1; c < N; ++c) {
             if (parent[c] != u) continue;
             has_child = 1;
             int x = draft[c];
-            softmax_T(p + (size_t)c * V, V, T, w->Pc);
+            if (!wor)
+                softmax_T(p + (size_t)c * V, V, T, w->Pc);
+            else if (variant == 2)
+                memcpy(w->Pc, w->Pu, sizeof(double) * (size_t)V);
+            else
+                without_replacement(w->Pu, drawn, nd, V, w->Pc);
             double px = w->Pc[x];
             double rx = (variant == 1) ? w->R0[x] : w->R[x];
             double a = (px == 0.0) ? 1.0 : fmin(1.0, rx / px);
@@ -210,6 +242,7 @@ static int walk_sampling(const float* q, const float* p, const int32_t* draft, c
                     w->R[v] = (t > 0.0) ? t / Z : 0.0;
                 }
             }
+            drawn[nd++] = x; /* at most N - 1 children */
         }
         if (!has_child || accepted < 0) break; /* leaf: bonus from P_q(u); else residual */
         acc_nodes[len] = accepted;
@@ -250,29 +283,41 @@ static int walk_greedy(const float* q, const int32_t* draft, const int32_t* pare
 
 /*
  * q_logits, p_logits: [B,N,V] fp32 (p may be NULL when greedy).  draft, parent:
- * [B,N].  Outputs: accept_len [B]; accepted_nodes, out_tokens [B,N], -1 padded;
- * nflags [B] near-boundary decision counts; min_margin [B] smallest distance
- * to a decision boundary (both may be NULL).
+ * [B,N].  seq_nodes: [B] nodes of each sequence (NULL: all N).  wor: siblings
+ * drawn without replacement (p row u is shared by u's children).  seq_offset:
+ * the Philox sequence counter of batch entry b is seq_offset + b.  Outputs:
+ * accept_len [B]; accepted_nodes, out_tokens [B,N], -1 padded; nflags [B]
+ * near-boundary decision counts; min_margin [B] smallest distance to a
+ * decision boundary (both may be NULL).
  */
-int orc_spec_accept(const float* q, const float* p, const int32_t* draft, const int32_t* parent,
-                    int B, int N, int V, uint64_t seed, double T, int greedy, int variant,
-                    int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
-                    int32_t* nflags, double* min_margin) {
+int orc_spec_accept_ex(const float* q, const float* p, const int32_t* draft, const int32_t* parent,
+                       const int32_t* seq_nodes, int B, int N, int V, uint64_t seed, double T, int greedy,
+                       int variant, int wor, uint32_t seq_offset, int32_t* accept_len, int32_t* accepted_nodes,
+                       int32_t* out_tokens, int32_t* nflags, double* min_margin) {
     if (B < 0 || N < 1 || V < 1 || !q || !draft || !parent || !accept_len || !accepted_nodes ||
         !out_tokens)
         return ORC_ERR_ARG;
     if (!greedy && (!p || !(T > 0.0) || !isfinite(T))) return ORC_ERR_ARG;
-    for (int b = 0; b < B; ++b)
-        if (!tree_is_valid(parent + (size_t)b * N, N)) return ORC_ERR_TREE;
-    for (int b = 0; b < B; ++b)
-        for (int c = 1; c < N; ++c)
+    for (int b = 0; b < B; ++b) {
+        int nb = seq_nodes ? seq_nodes[b] : N;
+        if (nb < 1 || nb > N) return ORC_ERR_ARG;
+        if (!tree_is_valid(parent + (size_t)b * N, nb)) return ORC_ERR_TREE;
+        for (int c = 1; c < nb; ++c)
             if (draft[(size_t)b * N + c] < 0 || draft[(size_t)b * N + c] >= V) return ORC_ERR_ARG;
+    }
     orc_scratch w;
-    w.R = (double*)malloc(sizeof(double) * (size_t)V * 3);
-    if (!w.R) return ORC_ERR_NOMEM;
+    w.R = (double*)malloc(sizeof(double) * (size_t)V * 4);
+    w.drawn = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+    if (!w.R || !w.drawn) {
+        free(w.R);
+        free(w.drawn);
+        return ORC_ERR_NOMEM;
+    }
     w.R0 = w.R + V;
     w.Pc = w.R + 2 * (size_t)V;
+    w.Pu = w.R + 3 * (size_t)V;
     for (int b = 0; b < B; ++b) {
+        int nb = seq_nodes ? seq_nodes[b] : N;
         int32_t* an = accepted_nodes + (size_t)b * N;
         int32_t* tk = out_tokens + (size_t)b * N;
         for (int i = 0; i < N; ++i) an[i] = tk[i] = -1;
@@ -280,14 +325,15 @@ int orc_spec_accept(const float* q, const float* p, const int32_t* draft, const 
         double margin = INFINITY;
         int len;
         if (greedy)
-            len = walk_greedy(q + (size_t)b * N * V, draft + (size_t)b * N, parent + (size_t)b * N, N, V,
+            len = walk_greedy(q + (size_t)b * N * V, draft + (size_t)b * N, parent + (size_t)b * N, nb, V,
                               an, tk);
         else
             len = walk_sampling(q + (size_t)b * N * V, p + (size_t)b * N * V, draft + (size_t)b * N,
-                                parent + (size_t)b * N, N, V, seed, (uint32_t)b, T, variant, &w, an, tk,
-                                &flags, &margin);
+                                parent + (size_t)b * N, nb, V, seed, seq_offset + (uint32_t)b, T, variant, wor,
+                                &w, an, tk, &flags, &margin);
         if (len < 0) {
             free(w.R);
+            free(w.drawn);
             return ORC_ERR_NOMEM;
         }
         accept_len[b] = len;
@@ -295,32 +341,52 @@ int orc_spec_accept(const float* q, const float* p, const int32_t* draft, const 
         if (min_margin) min_margin[b] = margin;
     }
     free(w.R);
+    free(w.drawn);
     return ORC_OK;
+}
+
+int orc_spec_accept(const float* q, const float* p, const int32_t* draft, const int32_t* parent,
+                    int B, int N, int V, uint64_t seed, double T, int greedy, int variant,
+                    int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
+                    int32_t* nflags, double* min_margin) {
+    return orc_spec_accept_ex(q, p, draft, parent, NULL, B, N, V, seed, T, greedy, variant, 0, 0u, accept_len,
+                              accepted_nodes, out_tokens, nflags, min_margin);
 }
 
 /*
  * Lossless harness (tests only): one sequence, fixed logits, ntrials Philox
  * seeds seed0 .. seed0+ntrials-1.  Per trial the draft token of every node c
- * is drawn from P_p(c) by inverse CDF with U(seed, c, 0, 2) (draft_mode 0) or
- * taken as argmax p_c (draft_mode 1), then the walk runs with the same seed.
- * Outputs per trial: drafts [ntrials,N], accept_len [ntrials],
- * accepted [ntrials,N], tokens [ntrials,N].
+ * is drawn by inverse CDF with U(seed, c, 0, 2):
+ *   draft_mode 0: from P_p(c) (independent siblings; walk with p row c);
+ *   draft_mode 1: taken as argmax p_c (negative control);
+ *   draft_mode 2: from P_p(parent(c)) without the tokens of c's earlier
+ *                 siblings, renormalised (walk in the without-replacement mode);
+ *   draft_mode 3: like 2 but with replacement (independent draws from the
+ *                 shared row), walked in the without-replacement mode.
+ * then the walk runs with the same seed.  Outputs per trial: drafts
+ * [ntrials,N], accept_len [ntrials], accepted [ntrials,N], tokens [ntrials,N].
  */
 int orc_lossless_trials(const float* q, const float* p, const int32_t* parent, int N, int V, double T,
                         uint64_t seed0, int64_t ntrials, int variant, int draft_mode, int32_t* drafts,
                         int32_t* accept_len, int32_t* accepted, int32_t* tokens) {
     if (N < 1 || V < 1 || !q || !p || !parent || !(T > 0.0)) return ORC_ERR_ARG;
     if (!tree_is_valid(parent, N)) return ORC_ERR_TREE;
+    const int wor = draft_mode >= 2;
     orc_scratch w;
-    w.R = (double*)malloc(sizeof(double) * (size_t)V * 3);
-    double* Pd = (double*)malloc(sizeof(double) * (size_t)V);
-    if (!w.R || !Pd) {
+    w.R = (double*)malloc(sizeof(double) * (size_t)V * 4);
+    double* Pd = (double*)malloc(sizeof(double) * (size_t)V * 2);
+    int32_t* sib = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+    w.drawn = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+    if (!w.R || !Pd || !sib || !w.drawn) {
         free(w.R);
         free(Pd);
+        free(sib);
+        free(w.drawn);
         return ORC_ERR_NOMEM;
     }
     w.R0 = w.R + V;
     w.Pc = w.R + 2 * (size_t)V;
+    w.Pu = w.R + 3 * (size_t)V;
     for (int64_t t = 0; t < ntrials; ++t) {
         uint64_t seed = seed0 + (uint64_t)t;
         int32_t* dr = drafts + t * N;
@@ -328,23 +394,37 @@ int orc_lossless_trials(const float* q, const float* p, const int32_t* parent, i
         int32_t* tk = tokens + t * N;
         dr[0] = 0;
         for (int c = 1; c < N; ++c) {
+            int dflags = 0;
+            double dmargin = INFINITY;
+            double ud = orc_uniform(seed, (uint32_t)c, 0u, 2u);
             if (draft_mode == 1) {
                 dr[c] = argmax_row(p + (size_t)c * V, V);
-            } else {
+            } else if (draft_mode == 0) {
                 softmax_T(p + (size_t)c * V, V, T, Pd);
-                int dflags = 0;
-                double dmargin = INFINITY;
-                dr[c] = sample_inverse_cdf(Pd, V, orc_uniform(seed, (uint32_t)c, 0u, 2u), &dflags,
-                                           &dmargin);
+                dr[c] = sample_inverse_cdf(Pd, V, ud, &dflags, &dmargin);
+            } else {
+                /* the earlier siblings of c, in index order */
+                int ns = 0;
+                for (int j = 1; j < c; ++j)
+                    if (parent[j] == parent[c]) sib[ns++] = dr[j];
+                softmax_T(p + (size_t)parent[c] * V, V, T, Pd);
+                if (draft_mode == 2) {
+                    without_replacement(Pd, sib, ns, V, Pd + V);
+                    dr[c] = sample_inverse_cdf(Pd + V, V, ud, &dflags, &dmargin);
+                } else {
+                    dr[c] = sample_inverse_cdf(Pd, V, ud, &dflags, &dmargin);
+                }
             }
         }
         for (int i = 0; i < N; ++i) an[i] = tk[i] = -1;
         int flags = 0;
         double margin = INFINITY;
-        accept_len[t] = walk_sampling(q, p, dr, parent, N, V, seed, 0u, T, variant, &w, an, tk, &flags,
+        accept_len[t] = walk_sampling(q, p, dr, parent, N, V, seed, 0u, T, variant, wor, &w, an, tk, &flags,
                                       &margin);
     }
     free(w.R);
     free(Pd);
+    free(sib);
+    free(w.drawn);
     return ORC_OK;
 }

@@ -45,15 +45,17 @@ def children_lists(parent_row):
     return ch
 
 
-def tree_mask(parent):
-    """parent: int array [B,N].
+def tree_mask(parent, seq_nodes=None):
+    """parent: int array [B,N]; seq_nodes: optional int [B], the nodes of each
+    sequence (the rest of its row is padding and is not read).
 
     Returns (anc, depth, status):
       anc    uint64 [B,N,W], W = ceil(N/64); bit j of word j//64 of anc[b,i]
              is set iff node j is i or an ancestor of i;
       depth  int32 [B,N], depth[root] = 0, depth[i] = depth[parent[i]] + 1;
       status int32 [B], 0 or BAD_TREE.  A sequence with an invalid parent
-             array gets all-zero bitsets and depth -1 throughout.
+             array gets all-zero bitsets and depth -1 throughout, and so do
+             the padding nodes of a ragged sequence.
     """
     parent = np.asarray(parent)
     B, N = parent.shape
@@ -62,10 +64,11 @@ def tree_mask(parent):
     depth = np.full((B, N), -1, dtype=np.int32)
     status = np.zeros(B, dtype=np.int32)
     for b in range(B):
-        if not tree_is_valid(parent[b]):
+        n = N if seq_nodes is None else int(seq_nodes[b])
+        if not 1 <= n <= N or not tree_is_valid(parent[b, :n]):
             status[b] = BAD_TREE
             continue
-        for i, s in enumerate(ancestor_sets(parent[b])):
+        for i, s in enumerate(ancestor_sets(parent[b, :n])):
             bits = 0
             for j in s:
                 bits |= 1 << j

@@ -124,3 +124,51 @@ def test_heads_subset_matches_full():
     part = oracle.tree_attention(Q, Kc, Vc, Kt, Vt, par, heads=[(1, 3), (0, 0)])
     assert np.array_equal(part[1, :, 3], full[1, :, 3]) and np.array_equal(part[0, :, 0], full[0, :, 0])
     assert np.isnan(part[0, :, 1]).all()
+
+
+@pytest.mark.parametrize("n", [65, 100, 128])
+def test_large_tree_equals_per_path_causal(n):
+    """Trees past one 64-bit ancestor word: every root-to-leaf path against
+    causal attention over [cache ; path]."""
+    rng = np.random.default_rng(n)
+    _check_per_path(random_tree(n, 9, 300 + n), rng, L=int(rng.integers(0, 20)), Hq=2, Hkv=1)
+
+
+def test_ragged_batch_equals_per_path_causal():
+    """Per-sequence node counts and cache lengths: each sequence's nodes see
+    only its own cache prefix and path (per-path causal attention via torch
+    SDPA); padding is never read."""
+    rng = np.random.default_rng(12)
+    B, N, Hq, Hkv, L, D = 4, 24, 4, 2, 30, 8
+    Q, Kc, Vc, Kt, Vt = _inputs(rng, B, N, Hq, Hkv, L, D)
+    nodes = np.array([24, 1, 9, 17])
+    lens = np.array([30, 0, 13, 1])
+    par = np.stack([random_tree(N, 6, 60 + b) for b in range(B)])
+    for b in range(B):  # poison the padding
+        par[b, nodes[b]:] = 1000
+        Kc[b, :, lens[b]:] = np.nan
+        Vc[b, :, lens[b]:] = np.nan
+        Kt[b, nodes[b]:] = np.nan
+        Vt[b, nodes[b]:] = np.nan
+        Q[b, nodes[b]:] = np.nan
+    out = oracle.tree_attention(Q, Kc, Vc, Kt, Vt, par, seq_nodes=nodes, seq_len=lens)
+    G = Hq // Hkv
+    for b in range(B):
+        n, lb = nodes[b], lens[b]
+        assert np.isnan(out[b, n:]).all() and np.isfinite(out[b, :n]).all()
+        ch = oracle.children_lists(par[b, :n])
+        for leaf in [i for i in range(n) if not ch[i]]:
+            path, j = [], leaf
+            while j != -1:
+                path.append(j)
+                j = par[b, j]
+            path = path[::-1]
+            P = len(path)
+            mask = np.zeros((P, lb + P), dtype=bool)
+            for a in range(P):
+                mask[a, : lb + a + 1] = True
+            for h in range(Hq):
+                k = np.concatenate([Kc[b, h // G, :lb], Kt[b, path, h // G]])
+                v = np.concatenate([Vc[b, h // G, :lb], Vt[b, path, h // G]])
+                ref = _sdpa(Q[b, path, h], k, v, mask)
+                np.testing.assert_allclose(out[b, path, h], ref, rtol=0, atol=1e-12)

@@ -98,3 +98,31 @@ def test_static_tree_matches_page():
     assert depth.max() == int(vals["depth"])
     widths = np.bincount(depth[0])
     assert widths.max() == int(vals["max_level_width"])
+
+
+def test_ragged_sequences_ignore_their_padding():
+    """Per-sequence node counts: the first n_b nodes get the mask of the
+    truncated tree (by pointer chasing here), the padding gets 0 / -1, and an
+    invalid parent inside the padding does not invalidate the sequence."""
+    N = 70
+    par = np.stack([random_tree(N, 8, 5), chain(N), random_tree(N, 3, 6)])
+    nodes = np.array([70, 1, 66])
+    par[1, 1:] = 55  # all padding, invalid if it were read
+    anc, depth, status = oracle.tree_mask(par, seq_nodes=nodes)
+    assert status.tolist() == [0, 0, 0]
+    for b in range(3):
+        n = nodes[b]
+        for i in range(N):
+            got = set()
+            for w in range(anc.shape[2]):
+                got |= {64 * w + j for j in _bits(anc[b, i, w])}
+            if i >= n:
+                assert not got and depth[b, i] == -1
+                continue
+            want, j = set(), i
+            while j != -1:
+                want.add(j)
+                j = int(par[b, j])
+            assert got == want and depth[b, i] == len(want) - 1
+    _, _, st = oracle.tree_mask(par, seq_nodes=np.array([70, 2, 66]))
+    assert st.tolist() == [0, oracle.tree.BAD_TREE, 0]
