@@ -23,9 +23,16 @@
  *  - Calls are stateless and deterministic for fixed inputs and seed.  Calls
  *    on different streams must not share a workspace.
  *
+ *  - Ragged batches: the _ex calls take seq_nodes [B] (nodes of each
+ *    sequence, 1..N; arrays keep the batch-wide stride N and the rest of a
+ *    sequence's rows is padding that is never read) and, for attention,
+ *    seq_len [B] (committed cache entries of each sequence, 0..L).  A NULL
+ *    array means every sequence uses all N nodes (all L entries).
+ *
  * Sources: the pages this library follows are cited per call by page and
- * section: the EAGLE explainer (0h-n0.github.io/posts/paper-2401-10774) and
- * the speculative-decoding survey explainer
+ * section: the EAGLE explainer (0h-n0.github.io/posts/paper-2401-10774), the
+ * EAGLE-3 explainer (0h-n0.github.io/posts/paper-2501-05370) and the
+ * speculative-decoding survey explainer
  * (0h-n0.github.io/posts/paper-2401-07851).
  */
 #ifndef TV_H_
@@ -41,14 +48,16 @@ extern "C" {
 typedef enum {
     TV_OK = 0,
     TV_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad temperature, ... */
-    TV_ERR_UNSUPPORTED = -2, /* valid but not implemented here: N > 64, D != 128 */
+    TV_ERR_UNSUPPORTED = -2, /* valid but not implemented here: N > TV_MAX_NODES, D != 128 */
     TV_ERR_BAD_TREE = -3,    /* parent[] violates the tree conventions (per-sequence status) */
     TV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query says */
     TV_ERR_HIP = -5          /* a HIP launch or runtime call failed */
 } tv_status;
 
-/* Largest tree (nodes including the root) handled: one 64-bit ancestor word per node. */
-#define TV_MAX_NODES 64
+/* Largest tree (nodes including the root) handled. */
+#define TV_MAX_NODES 256
+/* 64-bit ancestor words per node of an N-node tree: bit j % 64 of word j / 64. */
+#define TV_MASK_WORDS(N) (((N) + 63) / 64)
 /* Head dimension handled by the attention kernels. */
 #define TV_HEAD_DIM 128
 
@@ -65,17 +74,23 @@ int tv_version(void);
  * target pass with a tree attention mask verifies every root-to-node path, so
  * node i may see exactly its ancestors and itself.
  *
- *   parent     int32 [B,N]   parent index of each node (root: -1).
- *   anc_mask   uint64 [B,N]  out: bit j set iff node j is i or an ancestor of i.
- *   depth      int32 [B,N]   out: depth of each node (root 0); callers derive
- *                            rotary positions as L + depth.
- *   seq_status int32 [B]     out, may be NULL: 0, or TV_ERR_BAD_TREE when the
- *                            sequence's parent[] is invalid; such a sequence
- *                            gets anc_mask 0 and depth -1 throughout.
+ *   parent     int32 [B,N]     parent index of each node (root: -1).
+ *   anc_mask   uint64 [B,N,W]  out, W = TV_MASK_WORDS(N): bit j % 64 of word
+ *                              j / 64 set iff node j is i or an ancestor of i.
+ *   depth      int32 [B,N]     out: depth of each node (root 0); callers derive
+ *                              rotary positions as L + depth.
+ *   seq_status int32 [B]       out, may be NULL: 0, or TV_ERR_BAD_TREE when the
+ *                              sequence's parent[] is invalid (or, ragged, its
+ *                              node count is outside 1..N); such a sequence
+ *                              gets anc_mask 0 and depth -1 throughout.
  * Sizes: B >= 0 (B == 0 is a no-op), 1 <= N <= TV_MAX_NODES.
+ * tv_build_tree_mask_ex: ragged batches (seq_nodes may be NULL); padding nodes
+ * get anc_mask 0 and depth -1.
  */
 int tv_build_tree_mask(const int32_t* parent, int B, int N, uint64_t* anc_mask, int32_t* depth,
                        int32_t* seq_status, void* stream);
+int tv_build_tree_mask_ex(const int32_t* parent, const int32_t* seq_nodes, int B, int N, uint64_t* anc_mask,
+                          int32_t* depth, int32_t* seq_status, void* stream);
 
 /*
  * tv_tree_attention -- ancestor-masked attention of every tree node over the
@@ -95,13 +110,16 @@ int tv_build_tree_mask(const int32_t* parent, int B, int N, uint64_t* anc_mask, 
  *   V_cache  bf16 [B,Hkv,L,D]     committed values (may be NULL if L == 0).
  *   K_tree   bf16 [B,N,Hkv,D]     keys of the tree nodes.
  *   V_tree   bf16 [B,N,Hkv,D]     values of the tree nodes.
- *   anc_mask uint64 [B,N]         from tv_build_tree_mask; must describe a valid tree.
- *   out      fp32 [B,N,Hq,D]      out.
+ *   anc_mask uint64 [B,N,W]       from tv_build_tree_mask (W = TV_MASK_WORDS(N));
+ *                                 must describe a valid tree.
+ *   out      fp32 [B,N,Hq,D]      out (rows of padding nodes are not written).
  *   scale    softmax scale, conventionally 1/sqrt(D); finite and > 0.
  * Sizes: B >= 0, 1 <= N <= TV_MAX_NODES, Hq >= Hkv >= 1 with Hq % Hkv == 0,
- * D == TV_HEAD_DIM, L >= 0.
+ * D == TV_HEAD_DIM, L >= 0 (the cache's row stride; ragged calls read only the
+ * first seq_len[b] rows of sequence b).
  * Numerics: QK^T in bf16 with fp32 accumulation, softmax in fp32, P.V with
- * P and V in fp16 and fp32 accumulation.  Precondition: |V| <= 65504.
+ * P and V in fp16 and fp32 accumulation.  V values beyond the fp16 range
+ * (|v| > 65504) saturate to +-65504 in the P.V product.
  * Workspace: at least tv_tree_attention_workspace(...) bytes, 256-byte aligned
  * (may be NULL when that size is 0), zero-filled before its first use: when the
  * cache is split across workgroups it holds their partial results and one
@@ -113,6 +131,16 @@ int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t
                       const uint16_t* K_tree, const uint16_t* V_tree, const uint64_t* anc_mask,
                       float* out, int B, int N, int Hq, int Hkv, int D, int L, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+/* Ragged batches (survey explainer, open problems, batch inference: the
+ * sequences of a batch accept different numbers of drafts, so their caches
+ * and trees differ in length).  seq_nodes [B] and seq_len [B] may be NULL;
+ * values are taken as given (precondition 1 <= seq_nodes[b] <= N and
+ * 0 <= seq_len[b] <= L; others are clamped into those ranges). */
+int tv_tree_attention_ex(const uint16_t* Q, const uint16_t* K_cache, const uint16_t* V_cache,
+                         const uint16_t* K_tree, const uint16_t* V_tree, const uint64_t* anc_mask,
+                         float* out, const int32_t* seq_nodes, const int32_t* seq_len, int B, int N, int Hq,
+                         int Hkv, int D, int L, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * tv_spec_accept -- accept/reject walk over the tree (greedy or lossless
@@ -159,17 +187,55 @@ int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t
  * resident workgroup capacity).
  * Execution: one launch sized to the device's resident workgroup capacity;
  * every sequence is walked by a team of workgroups that synchronise through
- * the workspace, so calls that share a workspace must not overlap.  The
- * teams' waits assume that every workgroup of the launch runs at once (no
- * other work holds the device's compute units for long).  Each wait is
- * bounded (about a second); one that runs out lets the call finish, with
- * undefined outputs for that team's sequences.
+ * the workspace, so calls that share a workspace must not overlap, and calls
+ * on other streams (or other processes) that hold compute units for long can
+ * starve a team.  Each wait is bounded (about a second); when one runs out the
+ * call still finishes, and every sequence of that team reports accept_len -2
+ * (its other outputs undefined); the workspace stays reusable.
  */
 size_t tv_spec_accept_workspace(int B, int N, int V, int greedy);
 int tv_spec_accept(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
                    const int32_t* parent, int B, int N, int V, uint64_t philox_seed, float temperature,
                    int greedy, int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Flags of tv_spec_accept_ex. */
+#define TV_ACCEPT_GREEDY 1
+/* Siblings drawn without replacement (EAGLE explainer, static-tree
+ * verification: the children of a node are alternative candidates for the
+ * same position, taken from the draft's distribution at that node).  p row u
+ * is then the draft distribution AT node u, shared by u's children (rows of
+ * leaves are not read), and the children of u carry distinct tokens, child k
+ * drawn from that row with the tokens of children 1..k-1 removed.  Child k is
+ * tested against exactly that distribution; a rejection leaves
+ * norm(max(0, R - P^(k))).  Same lossless guarantee (survey explainer,
+ * classification of verification methods). */
+#define TV_ACCEPT_SIBLINGS_WOR 2
+
+/*
+ * tv_spec_accept_ex -- tv_spec_accept for ragged batches and without-
+ * replacement siblings.  seq_nodes [B] may be NULL; a sequence whose count is
+ * outside 1..N is reported like an invalid tree (accept_len -1).  flags:
+ * TV_ACCEPT_GREEDY and/or TV_ACCEPT_SIBLINGS_WOR (ignored when greedy).  The
+ * workspace is sized as for tv_spec_accept.
+ */
+int tv_spec_accept_ex(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
+                      const int32_t* parent, const int32_t* seq_nodes, int B, int N, int V, uint64_t philox_seed,
+                      float temperature, int flags, int32_t* accept_len, int32_t* accepted_nodes,
+                      int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The plan tv_spec_accept would use on the current device: workgroups per
+ * team (each owns one vocabulary slice of every row), teams, and the slice
+ * length.  Any output pointer may be NULL.  Host only. */
+int tv_spec_accept_plan(int B, int N, int V, int greedy, int* team_size, int* teams, int* slice);
+
+/* For tests and diagnostics: the number of polls each team wait of later
+ * accept calls makes before it gives up (process-wide).  0 makes every wait
+ * give up at once, so every sequence that needs its team reports -2;
+ * TV_WAIT_DEFAULT restores the default (about a second).  Returns the
+ * previous setting.  Host only. */
+#define TV_WAIT_DEFAULT 0xFFFFFFFFu
+uint32_t tv_set_wait_limit(uint32_t polls);
 
 /*
  * tv_philox_uniforms -- the uniforms tv_spec_accept draws, for auditing.

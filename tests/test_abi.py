@@ -29,7 +29,9 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("tv_build_tree_mask", "tv_tree_attention", "tv_spec_accept", "tv_tree_attention_workspace",
-              "tv_spec_accept_workspace", "tv_status_string", "tv_version", "tv_philox_uniforms"):
+              "tv_spec_accept_workspace", "tv_status_string", "tv_version", "tv_philox_uniforms",
+              "tv_build_tree_mask_ex", "tv_tree_attention_ex", "tv_spec_accept_ex", "tv_spec_accept_plan",
+              "tv_set_wait_limit"):
         assert n in names
 
 
@@ -50,7 +52,7 @@ def test_workspace_queries(lib):
     assert lib.tv_tree_attention_workspace(1, 6, 32, 8, 64, 4096) == 0     # unsupported head dim
     # the accept plan depends on the device's resident capacity: invalid shapes give 0 anywhere
     assert lib.tv_spec_accept_workspace(0, 6, 128256, 1) == 0
-    assert lib.tv_spec_accept_workspace(1, 65, 128256, 0) == 0
+    assert lib.tv_spec_accept_workspace(1, 257, 128256, 0) == 0
     assert lib.tv_spec_accept_workspace(1, 6, 0, 0) == 0
 
 
@@ -69,7 +71,7 @@ def test_attention_host_validation(lib):
     assert _attn(lib, N=0) == -1
     assert _attn(lib, Hq=30, Hkv=8) == -1
     assert _attn(lib, L=-2) == -1
-    assert _attn(lib, N=65) == -2
+    assert _attn(lib, N=257) == -2
     assert _attn(lib, D=64) == -2
     assert _attn(lib, scale=float("nan")) == -1
     assert _attn(lib, B=0) == 0
@@ -91,7 +93,7 @@ def _acc(lib, **kw):
 def test_accept_host_validation(lib):
     assert _acc(lib, B=-1) == -1
     assert _acc(lib, V=0) == -1
-    assert _acc(lib, N=65) == -2
+    assert _acc(lib, N=257) == -2
     assert _acc(lib, T=0.0) == -1
     assert _acc(lib, T=float("nan")) == -1
     assert _acc(lib, T=float("inf")) == -1
@@ -102,10 +104,26 @@ def test_accept_host_validation(lib):
     assert _acc(lib, greedy=1, T=0.0, p=0) == -4
 
 
+def test_accept_ex_host_validation(lib):
+    P = ctypes.c_void_p
+    lib.tv_spec_accept_ex.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                      ctypes.c_float, ctypes.c_int, P, P, P, P, ctypes.c_size_t, P]
+    call = lambda flags, sn=None: lib.tv_spec_accept_ex(P(256), P(256), P(256), P(256), sn, 1, 6, 100, 0, 1.0, flags,
+                                                        P(256), P(256), P(256), None, 0, None)
+    assert call(4) == -1          # unknown flag
+    assert call(3) == -4          # greedy | without replacement: valid, no workspace
+    assert call(2, P(256)) == -4  # ragged, without replacement
+    lib.tv_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.tv_set_wait_limit.restype = ctypes.c_uint32
+    prev = lib.tv_set_wait_limit(5)
+    assert lib.tv_set_wait_limit(0xFFFFFFFF) == 5
+    assert lib.tv_set_wait_limit(0xFFFFFFFF) == prev
+
+
 def test_mask_host_validation(lib):
     P = ctypes.c_void_p
     assert lib.tv_build_tree_mask(P(256), 1, 0, P(256), P(256), None, None) == -1
-    assert lib.tv_build_tree_mask(P(256), 1, 65, P(256), P(256), None, None) == -2
+    assert lib.tv_build_tree_mask(P(256), 1, 257, P(256), P(256), None, None) == -2
     assert lib.tv_build_tree_mask(None, 1, 4, P(256), P(256), None, None) == -1
     assert lib.tv_build_tree_mask(P(256), 0, 4, P(256), P(256), None, None) == 0
 

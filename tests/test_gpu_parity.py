@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import gpu_helpers as gh
 import oracle
 from workloads import CONFIGS, Workload, accept_inputs, attention_inputs, bf16_to_f64, chain, random_tree, \
     static_tree_60, tiny_workloads
@@ -67,7 +68,7 @@ def test_philox_bit_exact(tv):
 
 
 # -------------------------------------------------------------- tree mask --
-@pytest.mark.parametrize("N", [1, 2, 6, 17, 33, 60, 64])
+@pytest.mark.parametrize("N", [1, 2, 6, 17, 33, 60, 64, 65, 128, 200, 256])
 def test_tree_mask_bit_exact(tv, N):
     B = 48
     par = np.stack([random_tree(N, 1 + b % 9, 500 + b) for b in range(B)]).astype(np.int32)
@@ -81,14 +82,14 @@ def test_tree_mask_bit_exact(tv, N):
         par[5, N - 1] = -7
     anc, depth, status = tv.build_tree_mask(torch.from_numpy(par).to(dev()))
     o_anc, o_depth, o_status = oracle.tree_mask(par)
-    assert np.array_equal(_np(anc).view(np.uint64), o_anc[:, :, 0])
+    assert np.array_equal(_np(anc).view(np.uint64), o_anc)
     assert np.array_equal(_np(depth), o_depth)
     assert np.array_equal(_np(status), o_status)
 
 
 def test_tree_mask_empty_batch(tv):
     anc, depth, status = tv.build_tree_mask(torch.zeros((0, 5), dtype=torch.int32, device=dev()))
-    assert anc.shape == (0, 5)
+    assert anc.shape == (0, 5, 1)
 
 
 # -------------------------------------------------------------- attention --
@@ -162,29 +163,86 @@ def test_attention_deterministic(tv):
     assert torch.equal(out1, out2)
 
 
-def _sample_heads(w, k, seed):
-    rng = np.random.default_rng(seed)
-    pairs = {(0, 0), (w.B - 1, w.Hq - 1)}
-    while len(pairs) < k:
-        pairs.add((int(rng.integers(0, w.B)), int(rng.integers(0, w.Hq))))
-    return sorted(pairs)
-
-
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
-def test_attention_full_config_sampled(tv, name):
-    """Full-size inputs in the benchmark's launch configuration; the oracle
-    recomputes sampled (sequence, head) slices exactly."""
+def test_attention_full_config_whole(tv, name):
+    """Full-size inputs in the benchmark's launch configuration; the whole
+    output tensor against the fp64 oracle (every sequence and head)."""
     w = CONFIGS[name]
     (Q, Kc, Vc, Kt, Vt), par, out = _run_attention(tv, w)
-    G = w.G
-    for b, h in _sample_heads(w, 6, 3):
-        g = h // G
-        sl = lambda t, s: bf16_to_f64(t[b:b + 1, s]) if s is not None else bf16_to_f64(t[b:b + 1])
-        ref = oracle.tree_attention(bf16_to_f64(Q[b:b + 1, :, h:h + 1]), bf16_to_f64(Kc[b:b + 1, g:g + 1]),
-                                    bf16_to_f64(Vc[b:b + 1, g:g + 1]), bf16_to_f64(Kt[b:b + 1, :, g:g + 1]),
-                                    bf16_to_f64(Vt[b:b + 1, :, g:g + 1]), par[b:b + 1])
-        got = _np(out[b:b + 1, :, h:h + 1]).astype(np.float64)
-        _attn_check(got, ref, f"{name} b={b} h={h}")
+    got = _np(out).astype(np.float64)
+    ref = gh.oracle_attention(Q, Kc, Vc, Kt, Vt, par, label=name)
+    err, rel = _attn_check(got, ref, name)
+    gh.say(f"{name}: whole output {got.size} values, max abs {err:.2e}, rel L2 {rel:.2e}")
+
+
+# trees past one ancestor word: every kernel family (rows R = G*N up to 128 in
+# the small kernels, above in the wide one), ragged key tails, splits
+@pytest.mark.parametrize("B,N,Hq,Hkv,L", [
+    (2, 65, 1, 1, 70),      # R 65: 2x64 kernel, two tree tiles
+    (1, 100, 1, 1, 300),    # R 100: 2x64 kernel, two tree tiles
+    (2, 128, 2, 2, 129),    # R 128 per KV head: 2x64 kernel
+    (1, 256, 1, 1, 1000),   # R 256: wide kernel, four tree tiles
+    (2, 200, 4, 1, 2500),   # R 800: wide kernel, row tiles and splits
+    (1, 256, 8, 1, 0),      # no cache: tree tiles only
+])
+def test_attention_large_trees(tv, B, N, Hq, Hkv, L):
+    w = Workload("big", B=B, N=N, Hq=Hq, Hkv=Hkv, D=128, L=L, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),
+                 tree="random", max_depth=12, data_seed=N * 7 + L)
+    (Q, Kc, Vc, Kt, Vt), par, out = _run_attention(tv, w)
+    ref = oracle.tree_attention(*(bf16_to_f64(t) for t in (Q, Kc, Vc, Kt, Vt)), par)
+    _attn_check(_np(out).astype(np.float64), ref, f"B{B} N{N} Hq{Hq} Hkv{Hkv} L{L}")
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,L,nodes,lens", [
+    (4, 20, 4, 2, 300, [20, 1, 7, 13], [300, 0, 31, 64]),             # small kernels, one split
+    (4, 6, 4, 1, 4096, [6, 2, 6, 1], [4096, 100, 0, 4095]),           # many splits, some empty
+    (3, 64, 4, 1, 8192, [64, 30, 1], [8192, 63, 5000]),               # wide kernel, empty splits
+    (3, 130, 2, 1, 1500, [130, 65, 64], [1500, 700, 0]),              # two ancestor words, ragged
+])
+def test_attention_ragged(tv, B, N, Hq, Hkv, L, nodes, lens):
+    """Per-sequence node counts and cache lengths; padding rows of the output
+    are left as they were."""
+    w = Workload("rag", B=B, N=N, Hq=Hq, Hkv=Hkv, D=128, L=L, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),
+                 tree="random", max_depth=9, data_seed=N + L)
+    par = w.parents()
+    nodes, lens = np.array(nodes, np.int32), np.array(lens, np.int32)
+    for b in range(B):
+        par[b, nodes[b]:] = 10 ** 6  # padding is never read
+    Q, Kc, Vc, Kt, Vt = attention_inputs(w, device=dev())
+    sn, sl = torch.from_numpy(nodes).to(dev()), torch.from_numpy(lens).to(dev())
+    anc, _, st = tv.build_tree_mask(torch.from_numpy(par.astype(np.int32)).to(dev()), seq_nodes=sn)
+    assert (_np(st) == 0).all()
+    out = torch.full((B, N, Hq, 128), 7.0, dtype=torch.float32, device=dev())
+    tv.tree_attention(Q, Kc, Vc, Kt, Vt, anc, out=out, seq_nodes=sn, seq_len=sl)
+    torch.cuda.synchronize()
+    got = _np(out).astype(np.float64)
+    ref = oracle.tree_attention(*(bf16_to_f64(t) for t in (Q, Kc, Vc, Kt, Vt)), par, seq_nodes=nodes, seq_len=lens)
+    for b in range(B):
+        n = nodes[b]
+        assert (got[b, n:] == 7.0).all(), f"padding rows of sequence {b} were written"
+        _attn_check(got[b, :n], ref[b, :n], f"sequence {b} (nodes {n}, cache {lens[b]})")
+
+
+@pytest.mark.parametrize("L,N,Hq,Hkv", [(300, 17, 4, 2), (8192, 64, 8, 1)])
+def test_attention_values_beyond_fp16_saturate(tv, L, N, Hq, Hkv):
+    """V entries beyond the fp16 range enter the P.V product as +-65504 (the
+    output stays finite and matches the oracle on the saturated values)."""
+    w = Workload("sat", B=1, N=N, Hq=Hq, Hkv=Hkv, D=128, L=L, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),
+                 tree="random", max_depth=6, data_seed=5)
+    par = w.parents()
+    Q, Kc, Vc, Kt, Vt = attention_inputs(w, device=dev())
+    Vc[0, 0, 3, 5] = 1.0e6
+    Vc[0, 0, L - 1, 100] = -3.0e5
+    Vt[0, 2, 0, 7] = 2.0e5
+    anc, _, _ = tv.build_tree_mask(torch.from_numpy(par.astype(np.int32)).to(dev()))
+    got = _np(tv.tree_attention(Q, Kc, Vc, Kt, Vt, anc)).astype(np.float64)
+    sat = lambda t: np.clip(bf16_to_f64(t), -65504.0, 65504.0)
+    ref = oracle.tree_attention(bf16_to_f64(Q), bf16_to_f64(Kc), sat(Vc), bf16_to_f64(Kt), sat(Vt), par)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel <= RTOL_L2 and err <= ATOL * 65504.0 / 4.0, f"max abs {err:.3g}, rel L2 {rel:.3g}"
 
 
 # ----------------------------------------------------------------- accept --
@@ -351,22 +409,217 @@ def test_accept_full_config(tv, name):
     assert flips <= FLIP_RATE * nodes
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+SWEEP_SEEDS = {"c1": 1000, "c2": 1000, "c3": 1000, "c4": 16, "c5": 16}
+SWEEP = {}  # workload -> (draft nodes, flagged flips)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_accept_sampling_seed_sweep(tv, name):
-    """Many Philox seeds on a full-size configuration: the flagged-flip rate
-    must stay below 0.01% of draft nodes."""
+    """Philox seeds 0..999 on c1-c3 and 0..15 on c4-c5 (about 1.08e6 draft
+    nodes in all): bit-exact on every unflagged sequence.  The flagged-flip
+    rate is judged over the whole sweep (next test): one workload alone has
+    too few nodes for a 0.01% rate to mean anything (c2: 5000)."""
     w = CONFIGS[name]
     T = [t for t in w.temperatures if t > 0][0]
     q, p, draft, parent_t = accept_inputs(w, device=dev())
+    seeds = list(range(SWEEP_SEEDS[name]))
+    gpu = {}
+    for seed in seeds:
+        a, n, t = tv.spec_accept(q, p, draft, parent_t, seed=seed, temperature=T)
+        gpu[seed] = (a, n, t)
+    torch.cuda.synchronize()
+    gpu = {k: tuple(_np(x) for x in v) for k, v in gpu.items()}
     qn, pn, dn, parn = _np(q), _np(p), _np(draft), _np(parent_t)
-    nseeds = {"c1": 400, "c2": 400, "c3": 60}[name]
+    del q, p
+    ref = gh.oracle_accept_seeds(qn, pn, dn, parn, seeds, _t32(T), label=name)
+    flips = sum(_compare_walk(gpu[s], ref[s], False) for s in seeds)
+    flagged = sum(int((ref[s]["flags"] > 0).sum()) for s in seeds)
+    nodes = len(seeds) * w.B * (w.N - 1)
+    SWEEP[name] = (nodes, flips)
+    gh.say(f"{name}: {len(seeds)} seeds, {nodes} draft nodes, {flagged} flagged sequences, {flips} flagged flips")
+    assert flips <= 10 * FLIP_RATE * nodes + 1  # a gross excess shows per workload already
+
+
+def test_accept_sampling_sweep_flip_rate():
+    """Flagged flips over the whole seed sweep below 0.01% of its draft nodes."""
+    if set(SWEEP) != set(SWEEP_SEEDS):
+        pytest.skip("the seed sweep did not run on every workload in this session")
+    nodes = sum(n for n, _ in SWEEP.values())
+    flips = sum(f for _, f in SWEEP.values())
+    gh.say(f"seed sweep: {nodes} draft nodes, {flips} flagged flips ({flips / nodes:.2e} of nodes)")
+    assert nodes >= 1_000_000
+    assert flips < FLIP_RATE * nodes
+
+
+def _topk_sibling_drafts(p, parent):
+    """Distinct sibling tokens: the children of node u take the top tokens of
+    p row u in child order (EAGLE-style expansion)."""
+    B, N = parent.shape
+    draft = np.zeros((B, N), np.int32)
+    for b in range(B):
+        used = {}
+        for c in range(1, N):
+            u = int(parent[b, c])
+            if u not in used:
+                used[u] = list(np.argsort(-p[b, u], kind="stable"))
+            draft[b, c] = used[u].pop(0)
+    return draft
+
+
+@pytest.mark.parametrize("N,V,B", [(128, 3001, 3), (256, 2000, 2)])
+def test_accept_large_trees(tv, N, V, B):
+    rng = np.random.default_rng(N)
+    par = np.stack([random_tree(N, 10, 900 + b) for b in range(B)]).astype(np.int32)
+    q = rng.normal(scale=3.0, size=(B, N, V)).astype(np.float32)
+    p = (q[np.arange(B)[:, None], np.maximum(par, 0)] + rng.normal(size=(B, N, V))).astype(np.float32)
+    p[:, 0] = 0
+    draft = p.argmax(-1).astype(np.int32)
+    draft[:, 0] = 0
+    tq, tp, td, tpar = (torch.from_numpy(x).to(dev()) for x in (q, p, draft, par))
+    gpu = _accept_gpu(tv, tq, None, td, tpar, 0, 1.0, True)
+    _compare_walk(gpu, oracle.spec_accept(q, None, draft, par, greedy=True), True)
     flips = 0
-    for seed in range(nseeds):
-        gpu = _accept_gpu(tv, q, p, draft, parent_t, seed, T, False)
-        ref = oracle.spec_accept(qn, pn, dn, parn, seed=seed, temperature=_t32(T))
-        flips += _compare_walk(gpu, ref, False)
-    nodes = nseeds * w.B * (w.N - 1)
-    assert flips <= FLIP_RATE * nodes
+    for seed in range(12):
+        for T in (1.0, 0.6):
+            gpu = _accept_gpu(tv, tq, tp, td, tpar, seed, T, False)
+            flips += _compare_walk(gpu, oracle.spec_accept(q, p, draft, par, seed=seed, temperature=_t32(T)), False)
+    assert flips <= FLIP_RATE * 24 * B * (N - 1) + 1e-9
+
+
+@pytest.mark.parametrize("wor", [False, True])
+def test_accept_ragged(tv, wor):
+    """Per-sequence node counts (padding never read), greedy and sampling."""
+    rng = np.random.default_rng(21)
+    B, N, V = 6, 70, 4099
+    nodes = np.array([70, 1, 9, 64, 2, 33], np.int32)
+    par = np.stack([random_tree(N, 7, 30 + b) for b in range(B)]).astype(np.int32)
+    q = rng.normal(scale=3.0, size=(B, N, V)).astype(np.float32)
+    if wor:
+        p = (q + rng.normal(size=(B, N, V))).astype(np.float32)
+        draft = _topk_sibling_drafts(p, par)
+    else:
+        p = (q[np.arange(B)[:, None], np.maximum(par, 0)] + rng.normal(size=(B, N, V))).astype(np.float32)
+        draft = p.argmax(-1).astype(np.int32)
+    for b in range(B):
+        par[b, nodes[b]:] = 5000
+        draft[b, nodes[b]:] = -9
+    tq, tp, td, tpar, tn = (torch.from_numpy(x).to(dev()) for x in (q, p, draft, par, nodes))
+    for greedy in (True, False):
+        for seed in range(1 if greedy else 16):
+            a, n, t = tv.spec_accept(tq, None if greedy else tp, td, tpar, seed=seed, temperature=0.8, greedy=greedy,
+                                     seq_nodes=tn, wor=wor)
+            ref = oracle.spec_accept(q, None if greedy else p, draft, par, seed=seed, temperature=_t32(0.8),
+                                     greedy=greedy, seq_nodes=nodes, wor=wor)
+            _compare_walk((_np(a), _np(n), _np(t)), ref, greedy)
+
+
+@pytest.mark.parametrize("tree", ["static60", "random"])
+def test_accept_without_replacement(tv, tree):
+    """Siblings drawn without replacement from their parent's draft row: the
+    top tokens of that row (as EAGLE expands a node), and tokens sampled from
+    it without replacement."""
+    rng = np.random.default_rng(5)
+    B, N, V = 8, 60, 32000
+    par = (np.tile(static_tree_60(), (B, 1)) if tree == "static60"
+           else np.stack([random_tree(N, 6, 70 + b) for b in range(B)])).astype(np.int32)
+    q = rng.normal(scale=3.0, size=(B, N, V)).astype(np.float32)
+    p = (q + rng.normal(size=(B, N, V))).astype(np.float32)
+    drafts = [_topk_sibling_drafts(p, par)]
+    # sampled without replacement (numpy draws; the walk only sees the tokens)
+    d2 = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for u in range(N):
+            kids = [c for c in range(1, N) if par[b, c] == u]
+            if kids:
+                pr = np.exp(p[b, u].astype(np.float64) - p[b, u].max())
+                d2[b, kids] = rng.choice(V, size=len(kids), replace=False, p=pr / pr.sum())
+    drafts.append(d2)
+    tq, tp, tpar = (torch.from_numpy(x).to(dev()) for x in (q, p, par))
+    flips, nodes = 0, 0
+    for draft in drafts:
+        td = torch.from_numpy(draft).to(dev())
+        for seed in range(20):
+            a, n, t = tv.spec_accept(tq, tp, td, tpar, seed=seed, temperature=1.0, wor=True)
+            ref = oracle.spec_accept(q, p, draft, par, seed=seed, temperature=1.0, wor=True)
+            flips += _compare_walk((_np(a), _np(n), _np(t)), ref, False)
+            nodes += B * (N - 1)
+    assert flips <= FLIP_RATE * nodes + 1e-9
+
+
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_accept_wide_team_sampling(tv, B):
+    """Teams of more than 64 workgroups in sampling mode (the merge that
+    takes four members per lane and the multi-wave owner search)."""
+    N, V = 60, 128256
+    W, teams, _ = tv.accept_plan(B, N, V, False)
+    assert W > 64, f"plan gave {W} members"
+    w = Workload("wide", B=B, N=N, Hq=1, Hkv=1, D=128, L=1, V=V, sigma_q=3.0, sigma_n=1.0, temperatures=(1.0,),
+                 tree="random", max_depth=7, data_seed=40 + B)
+    q, p, draft, parent_t = accept_inputs(w, device=dev())
+    qn, pn, dn, parn = _np(q), _np(p), _np(draft), _np(parent_t)
+    flips = 0
+    for seed in range(10):
+        gpu = _accept_gpu(tv, q, p, draft, parent_t, seed, 1.0, False)
+        flips += _compare_walk(gpu, oracle.spec_accept(qn, pn, dn, parn, seed=seed, temperature=1.0), False)
+    assert flips <= FLIP_RATE * 10 * B * (N - 1) + 1e-9
+
+
+@pytest.mark.timeout(600)
+def test_accept_many_sequences_per_team(tv):
+    """Two-member teams (a vocabulary over one member's on-chip slice), each
+    verifying 18 sequences in one call (past the 16 sequence iterations the
+    walk's exchange tags distinguish), with star trees whose drafts the target
+    rarely agrees with, so that nearly every child is rejected and every
+    rejection is an exchange."""
+    N, V = 16, 32772
+    W, teams, _ = tv.accept_plan(1 << 20, N, V, False)
+    assert W == 2
+    B = teams * 18
+    par = np.tile(np.array([-1] + [0] * (N - 1), np.int32), (B, 1))
+    q = torch.randn((B, N, V), generator=torch.Generator(device=dev()).manual_seed(1), device=dev()) * 2.0
+    p = torch.randn((B, N, V), generator=torch.Generator(device=dev()).manual_seed(2), device=dev()) * 2.0
+    # each child drafts its own row's argmax, which the unrelated target rarely agrees with
+    draft = p.argmax(-1).to(torch.int32)
+    tpar = torch.from_numpy(par).to(dev())
+    a, n, t = tv.spec_accept(q, p, draft, tpar, seed=9, temperature=1.0)
+    torch.cuda.synchronize()
+    gpu = (_np(a), _np(n), _np(t))
+    qn, pn, dn = _np(q), _np(p), _np(draft)
+    del q, p
+    ref = gh.oracle_accept_chunks(qn, pn, dn, par, 9, 1.0, chunk=64, label="many-per-team")
+    flips = _compare_walk(gpu, ref, False)
+    assert flips <= FLIP_RATE * B * (N - 1) + 1e-9
+    assert (gpu[0] == 0).mean() > 0.5  # the drafts are mostly rejected
+
+
+def test_accept_failed_waits_are_reported(tv):
+    """A wait that gives up is reported: with the wait limit at 0 every team
+    wait gives up at once, every sequence reports accept_len -2 and every
+    kernel still exits; afterwards the same workspace gives exact results."""
+    w = CONFIGS["c3"]
+    q, p, draft, parent_t = accept_inputs(w, device=dev())
+    assert tv.accept_plan(w.B, w.N, w.V, False)[0] >= 2
+    need = max(tv.accept_workspace_bytes(w.B, w.N, w.V, g) for g in (0, 1))
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    prev = tv.set_wait_limit(0)
+    try:
+        for greedy in (False, True):
+            a, _, _ = tv.spec_accept(q, None if greedy else p, draft, parent_t, seed=1, temperature=0.7,
+                                     greedy=greedy, workspace=ws)
+            torch.cuda.synchronize()
+            assert (_np(a) == -2).all(), _np(a)
+    finally:
+        tv.set_wait_limit(prev)
+    qn, pn, dn, parn = _np(q), _np(p), _np(draft), _np(parent_t)
+    for greedy in (False, True):
+        for seed in range(3):
+            a, n, t = tv.spec_accept(q, None if greedy else p, draft, parent_t, seed=seed, temperature=0.7,
+                                     greedy=greedy, workspace=ws)
+            torch.cuda.synchronize()
+            ref = oracle.spec_accept(qn, None if greedy else pn, dn, parn, seed=seed, temperature=_t32(0.7),
+                                     greedy=greedy)
+            _compare_walk((_np(a), _np(n), _np(t)), ref, greedy)
 
 
 def test_graph_replay_matches_eager(tv):

@@ -6,13 +6,20 @@ hand-written HIP kernels for gfx950.  Tensors are torch device tensors; torch
 supplies memory and streams only.
 """
 from ._binding import (  # noqa: F401
+    ACCEPT_GREEDY,
+    ACCEPT_SIBLINGS_WOR,
     LIB_PATH,
+    TV_MAX_NODES,
+    WAIT_DEFAULT,
     TVError,
+    accept_plan,
     accept_workspace_bytes,
     attention_workspace_bytes,
     build_tree_mask,
     library,
+    mask_words,
     philox_uniforms,
+    set_wait_limit,
     spec_accept,
     tree_attention,
 )
@@ -21,6 +28,9 @@ __all__ = [
     "build_tree_mask",
     "tree_attention",
     "spec_accept",
+    "accept_plan",
+    "set_wait_limit",
+    "mask_words",
     "philox_uniforms",
     "attention_workspace_bytes",
     "accept_workspace_bytes",

@@ -44,14 +44,24 @@ def _load():
     lib.tv_version.restype = I
     lib.tv_build_tree_mask.argtypes = [P, I, I, P, P, P, P]
     lib.tv_build_tree_mask.restype = I
+    lib.tv_build_tree_mask_ex.argtypes = [P, P, I, I, P, P, P, P]
+    lib.tv_build_tree_mask_ex.restype = I
     lib.tv_tree_attention_workspace.argtypes = [I, I, I, I, I, I]
     lib.tv_tree_attention_workspace.restype = SZ
     lib.tv_tree_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P]
     lib.tv_tree_attention.restype = I
+    lib.tv_tree_attention_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P]
+    lib.tv_tree_attention_ex.restype = I
     lib.tv_spec_accept_workspace.argtypes = [I, I, I, I]
     lib.tv_spec_accept_workspace.restype = SZ
     lib.tv_spec_accept.argtypes = [P, P, P, P, I, I, I, U64, F, I, P, P, P, P, SZ, P]
     lib.tv_spec_accept.restype = I
+    lib.tv_spec_accept_ex.argtypes = [P, P, P, P, P, I, I, I, U64, F, I, P, P, P, P, SZ, P]
+    lib.tv_spec_accept_ex.restype = I
+    lib.tv_spec_accept_plan.argtypes = [I, I, I, I, P, P, P]
+    lib.tv_spec_accept_plan.restype = I
+    lib.tv_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.tv_set_wait_limit.restype = ctypes.c_uint32
     lib.tv_philox_uniforms.argtypes = [U64, P, I, P, P, P]
     lib.tv_philox_uniforms.restype = I
     _lib = lib
@@ -103,17 +113,39 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
-def build_tree_mask(parent: torch.Tensor):
-    """parent int32 [B,N] -> (anc_mask int64 [B,N] holding the uint64 bitsets,
+TV_MAX_NODES = 256
+ACCEPT_GREEDY = 1
+ACCEPT_SIBLINGS_WOR = 2
+WAIT_DEFAULT = 0xFFFFFFFF
+
+
+def mask_words(N: int) -> int:
+    return (N + 63) // 64
+
+
+def _seq_array(t: Optional[torch.Tensor], name: str, B: int, dev):
+    if t is None:
+        return None
+    _need(t, name, torch.int32, 1, dev)
+    if t.shape[0] != B:
+        raise ValueError(f"{name} must be [B]")
+    return t
+
+
+def build_tree_mask(parent: torch.Tensor, seq_nodes: Optional[torch.Tensor] = None):
+    """parent int32 [B,N] (seq_nodes: optional int32 [B] nodes per sequence) ->
+    (anc_mask int64 [B,N,W] holding the uint64 ancestor words, W = ceil(N/64),
     depth int32 [B,N], seq_status int32 [B])."""
     _need(parent, "parent", torch.int32, 2)
     B, N = parent.shape
     dev = parent.device
-    anc = torch.empty((B, N), dtype=torch.int64, device=dev)
+    sn = _seq_array(seq_nodes, "seq_nodes", B, dev)
+    anc = torch.empty((B, N, mask_words(N)), dtype=torch.int64, device=dev)
     depth = torch.empty((B, N), dtype=torch.int32, device=dev)
     status = torch.empty((B,), dtype=torch.int32, device=dev)
-    _check("tv_build_tree_mask",
-           _load().tv_build_tree_mask(_ptr(parent), B, N, _ptr(anc), _ptr(depth), _ptr(status), _stream(dev)))
+    _check("tv_build_tree_mask_ex",
+           _load().tv_build_tree_mask_ex(_ptr(parent), _ptr(sn), B, N, _ptr(anc), _ptr(depth), _ptr(status),
+                                         _stream(dev)))
     return anc, depth, status
 
 
@@ -122,22 +154,28 @@ def attention_workspace_bytes(B, N, Hq, Hkv, D, L) -> int:
 
 
 def tree_attention(Q, K_cache, V_cache, K_tree, V_tree, anc_mask, scale: Optional[float] = None,
-                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   seq_nodes: Optional[torch.Tensor] = None, seq_len: Optional[torch.Tensor] = None):
     """Q bf16 [B,N,Hq,D]; K/V_cache bf16 [B,Hkv,L,D]; K/V_tree bf16 [B,N,Hkv,D];
-    anc_mask int64 [B,N] -> out fp32 [B,N,Hq,D]."""
+    anc_mask int64 [B,N,W] (or [B,N] when N <= 64); optional seq_nodes,
+    seq_len int32 [B] for ragged batches -> out fp32 [B,N,Hq,D]."""
     _need(Q, "Q", torch.bfloat16, 4)
     dev = Q.device
     B, N, Hq, D = Q.shape
     for name, t in (("K_cache", K_cache), ("V_cache", V_cache), ("K_tree", K_tree), ("V_tree", V_tree)):
         _need(t, name, torch.bfloat16, 4, dev)
-    _need(anc_mask, "anc_mask", torch.int64, 2, dev)
+    if anc_mask.dim() == 2:
+        anc_mask = anc_mask.unsqueeze(-1)
+    _need(anc_mask, "anc_mask", torch.int64, 3, dev)
     Hkv, L = K_cache.shape[1], K_cache.shape[2]
     if tuple(K_cache.shape) != (B, Hkv, L, D) or tuple(V_cache.shape) != (B, Hkv, L, D):
         raise ValueError("K_cache/V_cache must be [B,Hkv,L,D]")
     if tuple(K_tree.shape) != (B, N, Hkv, D) or tuple(V_tree.shape) != (B, N, Hkv, D):
         raise ValueError("K_tree/V_tree must be [B,N,Hkv,D]")
-    if tuple(anc_mask.shape) != (B, N):
-        raise ValueError("anc_mask must be [B,N]")
+    if tuple(anc_mask.shape) != (B, N, mask_words(N)):
+        raise ValueError("anc_mask must be [B,N,ceil(N/64)]")
+    sn = _seq_array(seq_nodes, "seq_nodes", B, dev)
+    sl = _seq_array(seq_len, "seq_len", B, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -148,10 +186,10 @@ def tree_attention(Q, K_cache, V_cache, K_tree, V_tree, anc_mask, scale: Optiona
             raise ValueError("out must be [B,N,Hq,D]")
     ws = _workspace(attention_workspace_bytes(B, N, Hq, Hkv, D, L), dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check("tv_tree_attention",
-           _load().tv_tree_attention(_ptr(Q), _ptr(K_cache), _ptr(V_cache), _ptr(K_tree), _ptr(V_tree),
-                                     _ptr(anc_mask), _ptr(out), B, N, Hq, Hkv, D, L, float(scale), _ptr(ws), nbytes,
-                                     _stream(dev)))
+    _check("tv_tree_attention_ex",
+           _load().tv_tree_attention_ex(_ptr(Q), _ptr(K_cache), _ptr(V_cache), _ptr(K_tree), _ptr(V_tree),
+                                        _ptr(anc_mask), _ptr(out), _ptr(sn), _ptr(sl), B, N, Hq, Hkv, D, L,
+                                        float(scale), _ptr(ws), nbytes, _stream(dev)))
     return out
 
 
@@ -159,11 +197,27 @@ def accept_workspace_bytes(B, N, V, greedy) -> int:
     return int(_load().tv_spec_accept_workspace(B, N, V, int(bool(greedy))))
 
 
+def accept_plan(B, N, V, greedy):
+    """(team size, teams, slice length) that the accept call plans on the current device."""
+    w, t, sl = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check("tv_spec_accept_plan", _load().tv_spec_accept_plan(B, N, V, int(bool(greedy)), ctypes.byref(w),
+                                                               ctypes.byref(t), ctypes.byref(sl)))
+    return w.value, t.value, sl.value
+
+
+def set_wait_limit(polls: int) -> int:
+    """Polls each team wait of later accept calls makes (WAIT_DEFAULT restores
+    the default); returns the previous setting.  For tests and diagnostics."""
+    return int(_load().tv_set_wait_limit(int(polls) & 0xFFFFFFFF))
+
+
 def spec_accept(q_logits, p_logits, draft_tokens, parent, seed: int = 0, temperature: float = 1.0,
-                greedy: bool = False, workspace: Optional[torch.Tensor] = None, outputs=None):
+                greedy: bool = False, workspace: Optional[torch.Tensor] = None, outputs=None,
+                seq_nodes: Optional[torch.Tensor] = None, wor: bool = False):
     """q_logits/p_logits fp32 [B,N,V] (p may be None when greedy); draft_tokens,
-    parent int32 [B,N] -> (accept_len int32 [B], accepted_nodes int32 [B,N],
-    out_tokens int32 [B,N])."""
+    parent int32 [B,N]; optional seq_nodes int32 [B]; wor: siblings drawn
+    without replacement (p row u is the draft row at node u) ->
+    (accept_len int32 [B], accepted_nodes int32 [B,N], out_tokens int32 [B,N])."""
     _need(q_logits, "q_logits", torch.float32, 3)
     dev = q_logits.device
     B, N, V = q_logits.shape
@@ -175,18 +229,20 @@ def spec_accept(q_logits, p_logits, draft_tokens, parent, seed: int = 0, tempera
     _need(parent, "parent", torch.int32, 2, dev)
     if tuple(draft_tokens.shape) != (B, N) or tuple(parent.shape) != (B, N):
         raise ValueError("draft_tokens and parent must be [B,N]")
+    sn = _seq_array(seq_nodes, "seq_nodes", B, dev)
     if outputs is None:
         acc_len = torch.empty((B,), dtype=torch.int32, device=dev)
         acc_nodes = torch.empty((B, N), dtype=torch.int32, device=dev)
         toks = torch.empty((B, N), dtype=torch.int32, device=dev)
     else:
         acc_len, acc_nodes, toks = outputs
+    flags = (ACCEPT_GREEDY if greedy else 0) | (ACCEPT_SIBLINGS_WOR if wor else 0)
     ws = _workspace(accept_workspace_bytes(B, N, V, greedy), dev, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check("tv_spec_accept",
-           _load().tv_spec_accept(_ptr(q_logits), _ptr(p_logits), _ptr(draft_tokens), _ptr(parent), B, N, V,
-                                  int(seed) & 0xFFFFFFFFFFFFFFFF, float(temperature), int(bool(greedy)),
-                                  _ptr(acc_len), _ptr(acc_nodes), _ptr(toks), _ptr(ws), nbytes, _stream(dev)))
+    _check("tv_spec_accept_ex",
+           _load().tv_spec_accept_ex(_ptr(q_logits), _ptr(p_logits), _ptr(draft_tokens), _ptr(parent), _ptr(sn), B,
+                                     N, V, int(seed) & 0xFFFFFFFFFFFFFFFF, float(temperature), flags, _ptr(acc_len),
+                                     _ptr(acc_nodes), _ptr(toks), _ptr(ws), nbytes, _stream(dev)))
     return acc_len, acc_nodes, toks
 
 

@@ -44,9 +44,24 @@
 // seen every member's entries (every member read the word before streaming),
 // so nothing in the workspace needs clearing after it was zero-filled once.
 // The grid never exceeds the device's resident capacity, so all members of a
-// team run together; spins are bounded.
+// team run together; spins are bounded.  A wait that runs out is counted in
+// the workspace's arrival word; the last workgroup to finish (arrival count)
+// then reports every sequence of the teams concerned as failed
+// (accept_len -2) and moves their generation past every tag the call may have
+// written, so the workspace stays usable.
+//
+// Without-replacement siblings (EAGLE explainer, static-tree verification:
+// the children of a node are alternative candidates for the next position,
+// drawn from the draft's distribution at that node): p row u is then the
+// draft distribution at node u, shared by its children, and child k is tested
+// against it with the earlier (rejected) siblings' tokens removed and the rest
+// renormalised -- P^(k)(x) = P_u(x) / (1 - sum_j<k P_u(x_j)) -- and a rejection
+// leaves norm(max(0, R - P^(k))).  The residual already holds no mass at the
+// removed tokens (each was rejected with R < P there), so a pass needs only
+// the scale.
 #include <float.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "tv_device.h"
@@ -65,15 +80,16 @@ constexpr int kMaxSlice = 32768;     // sampling: a member's residual slice live
 constexpr int kMaxSpans = 4095;      // greedy: spans of 256 logits per slice, at most
 constexpr int kSpan = 4 * kWave;     // logits one wave covers with one 16-byte load per lane
 constexpr int kGroup = 4;            // spans per prefetch group (two groups in flight per wave)
-constexpr int kCtrlLine = 16;        // u64 words per team: [0] generation, [2] time-out flag
+constexpr int kCtrlLine = 16;        // u64 words per team: [0] generation, [2] a wait ran out in this call
 constexpr int kTagShift = 24;        // TeamSync::base = generation << kTagShift
-constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one wait (about a second)
+constexpr int kMaxNodes = TV_MAX_NODES;
 constexpr int kMassRec = 4;          // tagged u64 words per (pass, member): mass (two halves), new and old
                                      // residual at the next token
 
 struct AcceptPlan {
     int W, nteams, slice;
-    size_t ctrl_off, stats_off, mass_off, total;
+    size_t ctrl_off, done_off, stats_off, mass_off, total;
 };
 
 struct AccArgs {
@@ -81,13 +97,17 @@ struct AccArgs {
     const float* p;
     const int32_t* draft;
     const int32_t* parent;
+    const int32_t* seq_nodes;  // [B] nodes of each sequence, or null (all N)
     int32_t* accept_len;
     int32_t* accepted;
     int32_t* tokens;
     uint64_t* ctrl;      // [kMaxTeams][kCtrlLine]
+    uint64_t* done;      // arrivals of this call (low half), waits that ran out (high half)
     uint64_t* stats;     // [nteams][2][2N][W][2] tagged (max), (sum); greedy [nteams][2][N][W][2] (max), (index)
     double* mass;        // sampling: [nteams][N][W][kMassRec]
     int B, N, V, W, slice, nteams;
+    int wor;             // siblings drawn without replacement: p row u serves u's children
+    uint32_t spin_limit; // polls a wait makes before it gives up
     float c;             // log2(e) / T
     double inv_t64;      // 1 / T
     uint64_t seed;
@@ -104,23 +124,41 @@ __device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint
 
 struct TeamSync {
     uint64_t* line;    // this team's control line
+    uint64_t* done;    // the call's arrival word
     uint64_t base;     // (generation of this call) << kTagShift
-    uint32_t k;        // walk exchanges so far in this call
+    uint32_t limit;    // polls per wait
 };
 
-// Walk steps exchange tagged words: the tag is (generation << 12 | step) in
-// the upper 32 bits of every 64-bit word, so a word from an earlier step, or
-// from an earlier call, is told apart (a slot would have to go unused for 2^20
-// calls and then be reused at the same step to be mistaken).  Statistics
-// entries use (generation << 12 | sequence of the team) the same way.
-__device__ __forceinline__ uint32_t exchange_tag(TeamSync& s) {
-    ++s.k;
-    return (uint32_t)(((s.base >> kTagShift) << 12) | (s.k & 0xfffu));
+// A wait ran out: mark the team and count it in the arrival word (released,
+// so that the last workgroup, which acquires that word, sees the mark).  The
+// count's old value is consumed, so the wave does not go on before the
+// atomic has been performed.
+__device__ __forceinline__ void wait_failed(uint64_t* line, uint64_t* done) {
+    st_dev(&line[2], 1ull);
+    const uint64_t old = __hip_atomic_fetch_add(done, 1ull << 32, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" : : "v"(old));
 }
-// Poll one member's first nw words until all carry tag `tg` (upper half).
-__device__ __forceinline__ void gather_tagged(TeamSync& s, const uint64_t* src, uint64_t tg, int nw, uint64_t* e) {
-    uint32_t spins = 0;
-    for (;;) {
+
+// Walk steps exchange tagged words: the tag is (generation << 12 | sequence
+// iteration mod 16 << 8 | rejection pass) in the upper 32 bits of every 64-bit
+// word.  A slot is indexed by the pass, and the members of a team are never
+// more than one sequence apart during a walk (each needs every member's
+// statistics of its sequence first), so a word from an earlier sequence or
+// call is told apart (an older call would have to be 2^20 calls back).
+// Statistics entries use (generation << 12 | sequence of the team) the same
+// way.
+__device__ __forceinline__ uint32_t exchange_tag(const TeamSync& s, int iter, int pass) {
+    static_assert(kMaxNodes <= 257, "rejection passes of one walk fit eight bits");
+    return (uint32_t)(((s.base >> kTagShift) << 12) | ((uint32_t)(iter & 15) << 8) | (uint32_t)(pass & 255));
+}
+// Poll one member's first nw words until all carry tag `tg` (upper half); at
+// most s.limit polls (none when the limit is 0).
+__device__ __forceinline__ void gather_tagged(const TeamSync& s, const uint64_t* src, uint64_t tg, int nw, uint64_t* e) {
+    for (uint32_t polls = 0;; ++polls) {
+        if (polls >= s.limit) {
+            wait_failed(s.line, s.done);
+            return;
+        }
         bool ok = true;
 #pragma unroll
         for (int i = 0; i < kMassRec; ++i) {
@@ -130,17 +168,13 @@ __device__ __forceinline__ void gather_tagged(TeamSync& s, const uint64_t* src, 
         }
         if (ok) return;
         __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
-            st_dev(&s.line[2], 1ull);
-            return;
-        }
     }
 }
 
 // After the first merge of a call every member of the team has read the
 // team's generation word (before it streamed): member 0 advances it for the
 // next call.
-__device__ __forceinline__ void advance_generation(TeamSync& s, int w, bool& done) {
+__device__ __forceinline__ void advance_generation(const TeamSync& s, int w, bool& done) {
     if (!done && w == 0 && threadIdx.x == 0) st_dev(&s.line[0], s.base >> kTagShift);
     done = true;
 }
@@ -200,11 +234,13 @@ __device__ __forceinline__ double exp_scaled(float x, float m, double inv_t64, c
     return exp_nonpos(((double)x - (double)m) * inv_t64, tab);
 }
 
-// Storage index of the i-th streamed row: target rows 0..N-1, then draft rows
-// 1..N-1 stored at N + c.
-__device__ __forceinline__ int stat_row(int i, int N) { return i < N ? i : i + 1; }
+// Streamed rows are claimed in order i = 0, 1, ...; srow[i] (in LDS) is the
+// storage index of claim i: target row u at u, draft row k at N + k (N the
+// batch-wide node stride).  Target rows come first, then the draft rows the
+// walk may read: rows 1..n-1 (one per child), or, without replacement, the
+// rows of the nodes that have children.
 
-// Row pointer of a storage index: q row u at u, p row c at N + c.
+// Row pointer of a storage index.
 __device__ __forceinline__ const float* row_ptr(const float* qb, const float* pb, int r, int N, int V) {
     return r < N ? qb + (size_t)r * V : pb + (size_t)(r - N) * V;
 }
@@ -222,7 +258,7 @@ __device__ __forceinline__ const float* row_ptr(const float* qb, const float* pb
 template <bool GREEDY, bool VEC4>
 __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, int nrows, int N, int V, int s0,
                                               int nsl, float c, uint64_t* stats, int W, int w, int* rowctr,
-                                              uint64_t tg) {
+                                              uint64_t tg, const int* srow) {
     const int lane = threadIdx.x & 63;
     const int nspan = (nsl + kSpan - 1) / kSpan;
     auto take = [&]() -> int {
@@ -230,13 +266,13 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
         if (lane == 0) v = __hip_atomic_fetch_add(rowctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return __builtin_amdgcn_readfirstlane(v);
     };
-    static_assert(2 * TV_MAX_NODES <= 128 && kMaxSpans < 4096, "tag fields");
+    static_assert(2 * kMaxNodes <= 1024 && kMaxSpans < 4096, "tag fields");
     // load cursor: row li (claim index), span lj; past the last row the cursor
     // stays on its last span and marks the loads as fillers
     int li = take();
     int lj = 0;
     bool lvalid = li < nrows;
-    const float* lrow = row_ptr(qb, pb, stat_row(lvalid ? li : 0, N), N, V) + s0;
+    const float* lrow = row_ptr(qb, pb, srow[lvalid ? li : 0], N, V) + s0;
     auto load = [&](f32x4& x, int& xt) {
         const int e = lj * kSpan;
         if constexpr (VEC4) {
@@ -259,7 +295,7 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
             if (nxt < nrows) {
                 li = nxt;
                 lj = 0;
-                lrow = row_ptr(qb, pb, stat_row(li, N), N, V) + s0;
+                lrow = row_ptr(qb, pb, srow[li], N, V) + s0;
             } else {
                 lvalid = false;
                 lj = nspan - 1;
@@ -306,7 +342,7 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
             }
         }
         if (tag < 0) {  // the row's last span: reduce over the wave and publish
-            const int r = stat_row((tag >> 12) & 127, N);
+            const int r = srow[(tag >> 12) & 1023];
             if constexpr (GREEDY) {
                 group_argmax_dpp(bv, bi, kWave);
                 if (lane == 0) {
@@ -367,7 +403,7 @@ __device__ __forceinline__ int lanes_per_row(int W) {
 // members per lane and one group (16 rows per round trip).
 template <int KB, int PER>
 __device__ __forceinline__ void poll_entries(const uint64_t* stats, const uint32_t (&idx)[KB][PER], int nk, uint64_t tg,
-                                             uint64_t (&e)[KB][PER][2], uint64_t* line) {
+                                             uint64_t (&e)[KB][PER][2], const TeamSync& sync) {
     auto fetch = [&]() {
         bool ok = true;
 #pragma unroll
@@ -382,33 +418,44 @@ __device__ __forceinline__ void poll_entries(const uint64_t* stats, const uint32
         }
         return ok;
     };
-    bool ok = fetch();
-    uint32_t spins = 0;
+    bool ok = false;
+    uint32_t polls = 0;
+    if (sync.limit > 0) {
+        ok = fetch();
+        polls = 1;
+    } else {
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) e[k][i][0] = e[k][i][1] = 0;
+    }
     while (__ballot(!ok)) {
-        __builtin_amdgcn_s_sleep(1);
-        if (!ok) ok = fetch();
-        if (++spins > kSpinLimit) {
-            if (!ok) st_dev(&line[2], 1ull);
+        if (polls >= sync.limit) {
+            if (!ok) wait_failed(sync.line, sync.done);
             break;
         }
+        __builtin_amdgcn_s_sleep(1);
+        if (!ok) ok = fetch();
+        ++polls;
     }
 }
 
 // Row groups of a merge pass: group k of wave w starts at row
 // base + (k kWaves + w) rpw, so every wave takes a group before any takes a
 // second; a wave's groups past the last row are skipped (nk counts the
-// others).  Entry indices are r W + member (< 2^15), with rows past the last
+// others).  Entry indices are r W + member with r the storage index of the
+// claimed row (srow, or the claim itself when null), with rows past the last
 // and members past W clamped so that the loads stay unconditional.
 template <int KB, int PER>
-__device__ __forceinline__ int entry_indices(int base, int wave, int rpw, int g, int li, int lpr, int nrows, int N,
-                                             int W, bool storage_rows, uint32_t (&idx)[KB][PER]) {
+__device__ __forceinline__ int entry_indices(int base, int wave, int rpw, int g, int li, int lpr, int nrows,
+                                             int W, const int* srow, uint32_t (&idx)[KB][PER]) {
     int nk = 0;
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
         const int r0 = base + (k * kWaves + wave) * rpw;
         if (r0 < nrows) nk = k + 1;
         const int ri = min(r0 + g, nrows - 1);
-        const int r = storage_rows ? stat_row(ri, N) : ri;
+        const int r = srow ? srow[ri] : ri;
 #pragma unroll
         for (int i = 0; i < PER; ++i) idx[k][i] = (uint32_t)(r * W + min(li + lpr * i, W - 1));
     }
@@ -419,8 +466,8 @@ __device__ __forceinline__ int entry_indices(int base, int wave, int rpw, int g,
 // of every streamed row, from the entries [r][W].  The factors are fp32
 // (relative error ~1e-7), the sums fp64.
 template <int KB, int PER>
-__device__ __forceinline__ void merge_sampling_t(const uint64_t* stats, int nrows, int N, int W, float c, float* sM,
-                                                 double* sS, uint64_t tg, uint64_t* line) {
+__device__ __forceinline__ void merge_sampling_t(const uint64_t* stats, int nrows, const int* srow, int W, float c,
+                                                 float* sM, double* sS, uint64_t tg, const TeamSync& sync) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lpr = lanes_per_row(W);
@@ -428,10 +475,10 @@ __device__ __forceinline__ void merge_sampling_t(const uint64_t* stats, int nrow
     const int g = lane / lpr, li = lane % lpr;
     for (int base = 0; base < nrows; base += KB * kWaves * rpw) {
         uint32_t idx[KB][PER];
-        const int nk = entry_indices<KB, PER>(base, wave, rpw, g, li, lpr, nrows, N, W, true, idx);
+        const int nk = entry_indices<KB, PER>(base, wave, rpw, g, li, lpr, nrows, W, srow, idx);
         if (nk == 0) break;
         uint64_t e[KB][PER][2];
-        poll_entries<KB, PER>(stats, idx, nk, tg, e, line);
+        poll_entries<KB, PER>(stats, idx, nk, tg, e, sync);
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             if (k >= nk) break;
@@ -449,7 +496,7 @@ __device__ __forceinline__ void merge_sampling_t(const uint64_t* stats, int nrow
                 if (mk[i] != -INFINITY) S += (double)lo_f(e[k][i][1]) * (double)__builtin_amdgcn_exp2f((mk[i] - M) * c);
             S = group_sum_dpp(S, lpr);
             if (ri < nrows && li == 0) {
-                const int r = stat_row(ri, N);
+                const int r = srow[ri];
                 sM[r] = M;
                 sS[r] = S;
             }
@@ -457,18 +504,18 @@ __device__ __forceinline__ void merge_sampling_t(const uint64_t* stats, int nrow
     }
 }
 
-__device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows, int N, int W, float c, float* sM,
-                                               double* sS, uint64_t tg, uint64_t* line) {
+__device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows, const int* srow, int W, float c,
+                                               float* sM, double* sS, uint64_t tg, const TeamSync& sync) {
     if (W <= kWave)
-        merge_sampling_t<4, 1>(stats, nrows, N, W, c, sM, sS, tg, line);
+        merge_sampling_t<4, 1>(stats, nrows, srow, W, c, sM, sS, tg, sync);
     else
-        merge_sampling_t<1, kMaxTeamSize / kWave>(stats, nrows, N, W, c, sM, sS, tg, line);
+        merge_sampling_t<1, kMaxTeamSize / kWave>(stats, nrows, srow, W, c, sM, sS, tg, sync);
 }
 
 // Greedy: argmax of every target row 0..N-1 from the entries [r][W].
 template <int KB, int PER>
 __device__ __forceinline__ void merge_greedy_t(const uint64_t* stats, int N, int W, int* amax, uint64_t tg,
-                                               uint64_t* line) {
+                                               const TeamSync& sync) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lpr = lanes_per_row(W);
@@ -476,10 +523,10 @@ __device__ __forceinline__ void merge_greedy_t(const uint64_t* stats, int N, int
     const int g = lane / lpr, li = lane % lpr;
     for (int base = 0; base < N; base += KB * kWaves * rpw) {
         uint32_t idx[KB][PER];
-        const int nk = entry_indices<KB, PER>(base, wave, rpw, g, li, lpr, N, N, W, false, idx);
+        const int nk = entry_indices<KB, PER>(base, wave, rpw, g, li, lpr, N, W, nullptr, idx);
         if (nk == 0) break;
         uint64_t e[KB][PER][2];
-        poll_entries<KB, PER>(stats, idx, nk, tg, e, line);
+        poll_entries<KB, PER>(stats, idx, nk, tg, e, sync);
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             if (k >= nk) break;
@@ -496,11 +543,11 @@ __device__ __forceinline__ void merge_greedy_t(const uint64_t* stats, int N, int
 }
 
 __device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W, int* amax, uint64_t tg,
-                                             uint64_t* line) {
+                                             const TeamSync& sync) {
     if (W <= kWave)
-        merge_greedy_t<4, 1>(stats, N, W, amax, tg, line);
+        merge_greedy_t<4, 1>(stats, N, W, amax, tg, sync);
     else
-        merge_greedy_t<1, kMaxTeamSize / kWave>(stats, N, W, amax, tg, line);
+        merge_greedy_t<1, kMaxTeamSize / kWave>(stats, N, W, amax, tg, sync);
 }
 
 // --------------------------------------------------------- residual passes --
@@ -652,27 +699,31 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
     const int nsl = min(V, s0 + a.slice) - s0;
     const float c = a.c;
 
-    __shared__ int s_par[TV_MAX_NODES], s_draft[TV_MAX_NODES], s_path[TV_MAX_NODES], s_depth[TV_MAX_NODES];
-    __shared__ float s_gq[TV_MAX_NODES], s_gp[TV_MAX_NODES];
-    __shared__ float s_M[2 * TV_MAX_NODES];
-    __shared__ double s_S[2 * TV_MAX_NODES];
+    __shared__ int s_par[kMaxNodes], s_draft[kMaxNodes], s_path[kMaxNodes], s_depth[kMaxNodes];
+    __shared__ int s_srow[2 * kMaxNodes];  // storage index of each claimed row
+    __shared__ float s_gq[kMaxNodes], s_gp[kMaxNodes];
+    __shared__ float s_M[2 * kMaxNodes];
+    __shared__ double s_S[2 * kMaxNodes];
     // sampling: the member's slice of the current residual
     __shared__ __attribute__((aligned(16))) float s_res[GREEDY ? 4 : kMaxSlice];
     __shared__ double s_wt[kWaves];
     __shared__ double s_wtw[2][GREEDY ? 1 : kWaves];  // the walk's two sums per step
     __shared__ double s_mass[GREEDY ? 1 : kMaxTeamSize];
     __shared__ double s_tab[32];
-    __shared__ double s_rejZ[GREEDY ? 1 : TV_MAX_NODES];
-    __shared__ int s_rej[GREEDY ? 1 : TV_MAX_NODES];
+    __shared__ double s_rejZ[GREEDY ? 1 : kMaxNodes];
+    __shared__ float s_rejP[GREEDY ? 1 : kMaxNodes];
+    __shared__ int s_rej[GREEDY ? 1 : kMaxNodes];
+    __shared__ uint64_t s_bal[kMaxNodes / kWave];
     __shared__ float s_wx[2], s_nwx[2];
     __shared__ double s_oexcl, s_target;
-    __shared__ int s_ok, s_tok, s_owner, s_fallback, s_rowctr, s_hitw[kWaves], s_lastw[kWaves];
+    __shared__ int s_tok, s_owner, s_fallback, s_rowctr, s_nprow, s_last, s_hitw[kWaves], s_lastw[kWaves];
     __shared__ uint64_t s_base;
 
     if (tid < 32) exp2_table(s_tab, tid);
     TeamSync sync;
     sync.line = a.ctrl + (size_t)team * kCtrlLine;
-    sync.k = 0;
+    sync.done = a.done;
+    sync.limit = a.spin_limit;
     sync.base = 0;
     // this call's tags start above the team's last generation (read before
     // this member's first arrival; the load overlaps the first tree load)
@@ -681,34 +732,30 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
 
     int iter = 0;
     for (int b = team; b < a.B; b += a.nteams, ++iter) {
-        // ---- tree and drafts of this sequence ----
-        if (tid < kWave) {
-            int ok = 1;
-            if (tid < N) {
-                const int pr = a.parent[(size_t)b * N + tid];
-                int d = a.draft[(size_t)b * N + tid];
-                d = d < 0 ? 0 : (d >= V ? V - 1 : d);  // out-of-range drafts violate the precondition
-                s_par[tid] = pr;
-                s_draft[tid] = d;
-                ok = tid == 0 ? pr == -1 : (pr >= 0 && pr < tid);
-            }
-            const bool all_ok = __all(ok);
-            if (tid == 0) {
-                s_ok = all_ok;
-                s_rowctr = 0;  // every wave finished the previous stream (workgroup barriers followed it)
-            }
+        // ---- tree and drafts of this sequence (its first nb nodes) ----
+        const int nb = a.seq_nodes ? a.seq_nodes[b] : N;
+        int ok = nb >= 1 && nb <= N;
+        if (ok && tid < nb) {
+            const int pr = a.parent[(size_t)b * N + tid];
+            int d = a.draft[(size_t)b * N + tid];
+            d = d < 0 ? 0 : (d >= V ? V - 1 : d);  // out-of-range drafts violate the precondition
+            s_par[tid] = pr;
+            s_draft[tid] = d;
+            ok = tid == 0 ? pr == -1 : (pr >= 0 && pr < tid);
+            if (!GREEDY) s_depth[tid] = 0;  // sampling: marks nodes that have children (below)
         }
-        __syncthreads();
+        if (tid == 0) s_rowctr = 0;  // every wave finished the previous stream (workgroup barriers followed it)
+        const bool all_ok = __syncthreads_and(ok) != 0;
         int32_t* out_nodes = a.accepted + (size_t)b * N;
         int32_t* out_toks = a.tokens + (size_t)b * N;
-        if (!s_ok) {
+        if (!all_ok) {
             // every member sees the same tree: nobody streams or synchronises.
             // The sequence takes no statistics buffer (iter does not advance):
             // the next one reuses the buffer this one would have taken, so a
             // member never overwrites entries of the sequence before the last
             // one it merged, which another member may still be merging.
             if (w == 0) {
-                if (tid == 0) a.accept_len[b] = -1;
+                if (tid == 0) __hip_atomic_store(&a.accept_len[b], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 for (int i = tid; i < N; i += kThreads) {
                     out_nodes[i] = -1;
                     out_toks[i] = -1;
@@ -721,15 +768,50 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
 
         const float* qb = a.q + (size_t)b * N * V;
         const float* pb = GREEDY ? nullptr : a.p + (size_t)b * N * V;
-        // rows streamed: target rows 0..N-1, then (sampling) draft rows 1..N-1
-        const int nrows = GREEDY ? N : 2 * N - 1;
+        // ---- the rows to stream: target rows 0..nb-1, then (sampling) the
+        // draft rows: 1..nb-1, or without replacement the rows of the nodes
+        // that have children ----
+        int nrows = nb;
+        if (GREEDY) {
+            if (tid < nb) s_srow[tid] = tid;
+        } else if (!a.wor) {
+            if (tid < 2 * nb - 1) s_srow[tid] = tid < nb ? tid : N + (tid - nb + 1);
+            nrows = 2 * nb - 1;
+        } else {
+            // an opaque copy of the thread index: what is derived from it here is
+            // formed here, not held in registers across the sequence loop
+            int t = tid;
+            asm volatile("" : "+v"(t));
+            if (t >= 1 && t < nb) s_depth[s_par[t]] = 1;  // u has a child (same value from every writer)
+            __syncthreads();
+            const bool has = t < nb && s_depth[t] == 1;
+            if (t < kMaxNodes) {
+                const uint64_t bal = __ballot(has);
+                if ((t & (kWave - 1)) == 0) s_bal[t >> 6] = bal;
+            }
+            if (t < nb) s_srow[t] = t;
+            __syncthreads();
+            if (has) {
+                int rank = __popcll(s_bal[t >> 6] & ((1ull << (t & 63)) - 1ull));
+                for (int k = 0; k < (t >> 6); ++k) rank += __popcll(s_bal[k]);
+                s_srow[nb + rank] = N + t;
+            }
+            if (tid == 0) {
+                int tot = 0;
+                for (int k = 0; k < kMaxNodes / kWave; ++k) tot += __popcll(s_bal[k]);
+                s_nprow = tot;
+            }
+            __syncthreads();
+            nrows = nb + s_nprow;
+        }
+        __syncthreads();  // the row table is complete
         // gathered logits of the accept tests, in flight during the stream
         float gq = 0.f, gp = 0.f;
         const int gc = tid + 1;
-        if (!GREEDY && gc < N) {
+        if (!GREEDY && gc < nb) {
             const int x = s_draft[gc];
             gq = qb[(size_t)s_par[gc] * V + x];
-            gp = pb[(size_t)gc * V + x];
+            gp = pb[(size_t)(a.wor ? s_par[gc] : gc) * V + x];
         }
 
         // ---- 1. slice statistics of every row, published as entries tagged
@@ -745,12 +827,12 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
         }
         const uint64_t stag = (uint64_t)(uint32_t)(((sync.base >> kTagShift) << 12) | ((uint32_t)iter & 0xfffu)) << 32;
         uint64_t* stats = a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)2 * (GREEDY ? N : 2 * N) * W;
-        stream_slices<GREEDY, VEC4>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag);
+        stream_slices<GREEDY, VEC4>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag, s_srow);
         if constexpr (GREEDY) {
             // ---- 2. every member merges (seeing every member's entries), member 0
             // writes the path ----
             int* s_amax = s_path;  // reuse: argmax per target row
-            merge_greedy(stats, N, W, s_amax, stag, sync.line);
+            merge_greedy(stats, nb, W, s_amax, stag, sync);
             __syncthreads();
             advance_generation(sync, w, gen_done);
             if (w != 0) continue;
@@ -758,54 +840,76 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 out_nodes[i] = -1;
                 out_toks[i] = -1;
             }
+            // match(i): node i's draft equals its parent's argmax; valid(i): every
+            // node on the root-to-i path matches.  The end node is the deepest
+            // valid node, ties to the smallest index.
+            if (tid < nb) s_depth[tid] = tid == 0 ? 1 : (s_draft[tid] == s_amax[s_par[tid]]);
+            __syncthreads();
+            float key = -1.f;
+            int kidx = tid;
+            if (tid < nb) {
+                int d = 0;
+                bool v = true;
+                for (int j = tid; j != 0; j = s_par[j]) {
+                    v = v && s_depth[j] != 0;
+                    ++d;
+                }
+                key = v ? (float)d : -1.f;
+            }
+            group_argmax_dpp(key, kidx, kWave);
+            if ((tid & (kWave - 1)) == 0) {
+                s_hitw[tid >> 6] = kidx;
+                s_wt[tid >> 6] = key;
+            }
             __syncthreads();
             if (tid == 0) {
-                // valid(i): every draft on the root-to-i path equals its parent's argmax
-                uint64_t ok = 1ull;
-                s_depth[0] = 0;
-                int e = 0;
-                for (int i = 1; i < N; ++i) {
-                    const int pr = s_par[i];
-                    s_depth[i] = s_depth[pr] + 1;
-                    if (((ok >> pr) & 1ull) && s_draft[i] == s_amax[pr]) {
-                        ok |= 1ull << i;
-                        if (s_depth[i] > s_depth[e]) e = i;
-                    }
-                }
-                const int len = s_depth[e];
+                float bk = s_wt[0];
+                int e = s_hitw[0];
+                for (int k = 1; k < kWaves; ++k) argmax_merge(bk, e, (float)s_wt[k], s_hitw[k]);
+                const int len = (int)bk;
                 for (int i = e, k = len - 1; i != 0; i = s_par[i], --k) {
                     out_nodes[k] = i;
                     out_toks[k] = s_draft[i];
                 }
                 out_toks[len] = s_amax[e];
-                a.accept_len[b] = len;
+                __hip_atomic_store(&a.accept_len[b], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
         } else {
             // ---- 3. every member merges every row ----
-            if (gc < N) {
+            if (gc < nb) {
                 s_gq[gc] = gq;
                 s_gp[gc] = gp;
             }
-            merge_sampling(stats, nrows, N, W, c, s_M, s_S, stag, sync.line);
+            merge_sampling(stats, nrows, s_srow, W, c, s_M, s_S, stag, sync);
             __syncthreads();
             advance_generation(sync, w, gen_done);
 
             // ---- the walk (identical on every member) ----
             const double inv_t64 = a.inv_t64;
+            const bool wor = a.wor != 0;
             double* massb = a.mass + (size_t)team * N * W * kMassRec;
             int u = 0, len = 0, pass = 0, nrej = 0;
             bool res_active = false;  // target at u: residual s_res / Z, else softmax(q_u / T)
             double Z = 1.0, wx_cur = 0.0;
+            double zrem = 1.0;        // without replacement: draft mass at u not yet drawn
             int c_cur = 1;
             for (;;) {
-                while (c_cur < N && s_par[c_cur] != u) ++c_cur;
-                if (c_cur >= N) break;  // every child of u tried, or u is a leaf
+                while (c_cur < nb && s_par[c_cur] != u) ++c_cur;
+                if (c_cur >= nb) break;  // every child of u tried, or u is a leaf
                 const int cc = c_cur;
+                const int pr_c = wor ? u : cc;  // the draft row cc was drawn from
+                const double pfull = exp_scaled(s_gp[cc], s_M[N + pr_c], inv_t64, s_tab) / s_S[N + pr_c];
                 {
                     const double rx = res_active ? wx_cur / Z
                                                  : exp_scaled(s_gq[cc], s_M[u], inv_t64, s_tab) / s_S[u];
-                    const double px = exp_scaled(s_gp[cc], s_M[N + cc], inv_t64, s_tab) / s_S[N + cc];
+                    double px = pfull;
+                    if (wor) {
+                        // a token already drawn by an earlier sibling has no mass left
+                        bool dup = false;
+                        for (int j = u + 1; j < cc; ++j) dup = dup || (s_par[j] == u && s_draft[j] == s_draft[cc]);
+                        px = (dup || !(zrem > 0.0)) ? 0.0 : pfull / zrem;
+                    }
                     const double acc = px == 0.0 ? 1.0 : fmin(1.0, rx / px);
                     const double r = (double)philox_uniform(a.seed, (uint32_t)cc, (uint32_t)b, 0u);
                     if (r < acc) {
@@ -815,6 +919,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                         c_cur = u + 1;
                         res_active = false;
                         Z = 1.0;
+                        zrem = 1.0;
                         nrej = 0;
                         continue;
                     }
@@ -825,21 +930,23 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 // slice), so s_wx needs no reset.  Barriers: the two sums (each on
                 // its own array, so no leading barrier) ----
                 int nxt = cc + 1;
-                while (nxt < N && s_par[nxt] != u) ++nxt;
-                const int x2 = nxt < N ? s_draft[nxt] - s0 : -1;
+                while (nxt < nb && s_par[nxt] != u) ++nxt;
+                const int x2 = nxt < nb ? s_draft[nxt] - s0 : -1;
                 const int x2l = (x2 >= 0 && x2 < nsl) ? x2 : -1;
                 const float Mq = s_M[u];
                 const float invSq = (float)(1.0 / s_S[u]);
                 const float invZ = (float)(1.0 / Z);
+                const float invSp = (float)(1.0 / (s_S[N + pr_c] * zrem));
                 const float* q_u = qb + (size_t)u * V + s0;
-                const double part = residual_pass<VEC4>(res_active ? nullptr : q_u, pb + (size_t)cc * V + s0, Mq,
-                                                        invSq, s_M[N + cc], (float)(1.0 / s_S[N + cc]), invZ, c,
-                                                        nsl, s_res, x2l, &s_wx[1], &s_wx[0]);
+                const float* p_c = pb + (size_t)pr_c * V + s0;
+                const double part = residual_pass<VEC4>(res_active ? nullptr : q_u, p_c, Mq, invSq, s_M[N + pr_c],
+                                                        invSp, invZ, c, nsl, s_res, x2l, &s_wx[1], &s_wx[0]);
+                if (wor) zrem -= pfull;
                 const double smass = block_sum_1b(part, s_wtw[0]);  // its barrier publishes s_wx
                 // publish and gather in one step: every word carries the step's tag,
                 // so a member polls the other members' words directly
                 uint64_t* slot = reinterpret_cast<uint64_t*>(massb + (size_t)pass * W * kMassRec);
-                const uint64_t tg = (uint64_t)exchange_tag(sync) << 32;
+                const uint64_t tg = (uint64_t)exchange_tag(sync, iter, pass) << 32;
                 if (tid == 0) {
                     const uint64_t mb = (uint64_t)__double_as_longlong(smass);
                     st_dev(&slot[w * kMassRec + 0], tg | (uint32_t)mb);
@@ -847,7 +954,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                     st_dev(&slot[w * kMassRec + 2], tg | __float_as_uint(s_wx[0]));  // new residual at the next token
                     st_dev(&slot[w * kMassRec + 3], tg | __float_as_uint(s_wx[1]));  // stored residual before the pass
                 }
-                const int xo = nxt < N ? s_draft[nxt] / a.slice : -1;
+                const int xo = nxt < nb ? s_draft[nxt] / a.slice : -1;
                 double mt = 0.0;
                 if (tid < W) {
                     // the residuals at the next token only from the member that owns it
@@ -866,6 +973,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                     if (tid == 0) {
                         s_rej[nrej] = cc;
                         s_rejZ[nrej] = Znew;
+                        s_rejP[nrej] = invSp;
                     }
                     ++nrej;
                     res_active = true;
@@ -878,10 +986,10 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                     __syncthreads();
                     for (int k = 0; k < nrej; ++k) {
                         const int ck = s_rej[k];
+                        const int pk = wor ? u : ck;
                         const float iz = (float)(1.0 / (k == 0 ? 1.0 : s_rejZ[k - 1]));
-                        residual_pass<VEC4>(k == 0 ? q_u : nullptr, pb + (size_t)ck * V + s0, Mq, invSq,
-                                            s_M[N + ck], (float)(1.0 / s_S[N + ck]), iz, c, nsl, s_res, -1,
-                                            &s_wx[1], &s_wx[1]);
+                        residual_pass<VEC4>(k == 0 ? q_u : nullptr, pb + (size_t)pk * V + s0, Mq, invSq, s_M[N + pk],
+                                            s_rejP[k], iz, c, nsl, s_res, -1, &s_wx[1], &s_wx[1]);
                     }
                 }
                 c_cur = cc + 1;
@@ -971,17 +1079,42 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                     out_nodes[i] = i < len ? s_path[i] : -1;
                     out_toks[i] = i < len ? s_draft[s_path[i]] : (i == len ? s0 + tok : -1);
                 }
-                if (tid == 0) a.accept_len[b] = len;
+                if (tid == 0) __hip_atomic_store(&a.accept_len[b], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else if (owner < 0 && w == 0) {
                 // no mass anywhere (only possible with non-finite logits): last token
                 for (int i = tid; i < N; i += kThreads) {
                     out_nodes[i] = i < len ? s_path[i] : -1;
                     out_toks[i] = i < len ? s_draft[s_path[i]] : (i == len ? V - 1 : -1);
                 }
-                if (tid == 0) a.accept_len[b] = len;
+                if (tid == 0) __hip_atomic_store(&a.accept_len[b], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
         }  // sampling
+    }
+
+    // ---- arrival: the last workgroup reports the teams whose waits ran out.
+    // Each workgroup's accept_len stores are made by its thread 0 before this
+    // release; a wait that ran out released its team mark with its count ----
+    __syncthreads();
+    if (tid == 0) {
+        const uint64_t old = __hip_atomic_fetch_add(a.done, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = (uint32_t)old == gridDim.x - 1;
+        s_last = last ? ((old >> 32) != 0 ? 2 : 1) : 0;
+        if (last) st_dev(a.done, 0ull);  // every workgroup has arrived: ready for the next call
+    }
+    __syncthreads();
+    if (s_last == 2) {
+        for (int t = tid; t < a.nteams; t += kThreads) {
+            uint64_t* line = a.ctrl + (size_t)t * kCtrlLine;
+            if (ld_dev(&line[2]) == 0) continue;
+            for (int bb = t; bb < a.B; bb += a.nteams)
+                __hip_atomic_store(&a.accept_len[bb], -2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // members may have tagged words with this call's generation or the
+            // next one (a member that read the word after member 0 advanced it):
+            // the next call starts past both
+            st_dev(&line[0], ld_dev(&line[0]) + 2);
+            st_dev(&line[2], 0ull);
+        }
     }
 }
 
@@ -1074,11 +1207,71 @@ int make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
     size_t off = 0;
     pl.ctrl_off = off;
     off += round_up((size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t), 256);
+    pl.done_off = off;
+    off += 256;
     pl.stats_off = off;
     off += round_up((size_t)nteams * 2 * 2 * (greedy ? N : 2 * N) * W * sizeof(uint64_t), 256);
     pl.mass_off = off;
     if (!greedy) off += round_up((size_t)nteams * N * W * kMassRec * sizeof(double), 256);
     pl.total = off;
+    return TV_OK;
+}
+
+std::atomic<uint32_t> g_wait_limit{kSpinLimit};
+
+// Host checks and the launch; `ws` holds at least pl.total bytes.
+int launch_accept(const float* q_logits, const float* p_logits, const int32_t* draft_tokens, const int32_t* parent,
+                  const int32_t* seq_nodes, int B, int N, int V, uint64_t philox_seed, float temperature, int flags,
+                  int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens, char* ws, const AcceptPlan& pl,
+                  hipStream_t stream) {
+    const bool greedy = (flags & TV_ACCEPT_GREEDY) != 0;
+    AccArgs a;
+    a.q = q_logits;
+    a.p = p_logits;
+    a.draft = draft_tokens;
+    a.parent = parent;
+    a.seq_nodes = seq_nodes;
+    a.accept_len = accept_len;
+    a.accepted = accepted_nodes;
+    a.tokens = out_tokens;
+    a.ctrl = reinterpret_cast<uint64_t*>(ws + pl.ctrl_off);
+    a.done = reinterpret_cast<uint64_t*>(ws + pl.done_off);
+    a.stats = reinterpret_cast<uint64_t*>(ws + pl.stats_off);
+    a.mass = greedy ? nullptr : reinterpret_cast<double*>(ws + pl.mass_off);
+    a.B = B;
+    a.N = N;
+    a.V = V;
+    a.W = pl.W;
+    a.slice = pl.slice;
+    a.nteams = pl.nteams;
+    a.wor = (!greedy && (flags & TV_ACCEPT_SIBLINGS_WOR)) ? 1 : 0;
+    a.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
+    a.c = greedy ? 1.f : (float)(1.4426950408889634 / (double)temperature);
+    a.inv_t64 = greedy ? 1.0 : 1.0 / (double)temperature;
+    a.seed = philox_seed;
+    const bool vec4 = (V % 4 == 0) && aligned(q_logits, 16) && (greedy || aligned(p_logits, 16));
+    // The grid never exceeds the resident capacity from the occupancy query, so
+    // once earlier work on the stream drains every member is resident and the
+    // polls for other members' words make progress (their waits are bounded
+    // regardless, and one that runs out is reported as accept_len -2).
+    hipLaunchKernelGGL(pick(greedy, vec4), dim3(pl.nteams * pl.W), dim3(kThreads), 0, stream, a);
+    return launch_status();
+}
+
+// Argument checks shared by the entry points: TV_OK or a tv_status.
+int check_accept_args(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
+                      const int32_t* parent, int B, int N, int V, float temperature, int flags, int32_t* accept_len,
+                      int32_t* accepted_nodes, int32_t* out_tokens) {
+    const bool greedy = (flags & TV_ACCEPT_GREEDY) != 0;
+    if (B < 0 || N < 1 || V < 1) return TV_ERR_INVALID_ARG;
+    if ((flags & ~(TV_ACCEPT_GREEDY | TV_ACCEPT_SIBLINGS_WOR)) != 0) return TV_ERR_INVALID_ARG;
+    if (N > TV_MAX_NODES) return TV_ERR_UNSUPPORTED;
+    if (!greedy && !(temperature > 0.f && temperature <= FLT_MAX)) return TV_ERR_INVALID_ARG;
+    if (B == 0) return TV_OK;
+    if (!q_logits || (!greedy && !p_logits) || !draft_tokens || !parent || !accept_len || !accepted_nodes ||
+        !out_tokens)
+        return TV_ERR_INVALID_ARG;
+    if (!aligned(q_logits, 4) || (!greedy && !aligned(p_logits, 4))) return TV_ERR_INVALID_ARG;
     return TV_OK;
 }
 
@@ -1092,53 +1285,47 @@ extern "C" size_t tv_spec_accept_workspace(int B, int N, int V, int greedy) {
     return pl.total;
 }
 
+extern "C" int tv_spec_accept_plan(int B, int N, int V, int greedy, int* team_size, int* teams, int* slice) {
+    if (B <= 0 || N < 1 || N > TV_MAX_NODES || V < 1) return TV_ERR_INVALID_ARG;
+    tv::AcceptPlan pl;
+    const int st = tv::make_plan(B, N, V, greedy, pl);
+    if (st != TV_OK) return st;
+    if (team_size) *team_size = pl.W;
+    if (teams) *teams = pl.nteams;
+    if (slice) *slice = pl.slice;
+    return TV_OK;
+}
+
+extern "C" uint32_t tv_set_wait_limit(uint32_t polls) {
+    return tv::g_wait_limit.exchange(polls == TV_WAIT_DEFAULT ? tv::kSpinLimit : polls);
+}
+
+extern "C" int tv_spec_accept_ex(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
+                                 const int32_t* parent, const int32_t* seq_nodes, int B, int N, int V,
+                                 uint64_t philox_seed, float temperature, int flags, int32_t* accept_len,
+                                 int32_t* accepted_nodes, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    using namespace tv;
+    int st = check_accept_args(q_logits, p_logits, draft_tokens, parent, B, N, V, temperature, flags, accept_len,
+                               accepted_nodes, out_tokens);
+    if (st != TV_OK || B == 0) return st;
+    if (!workspace || !aligned(workspace, 256)) return TV_ERR_WORKSPACE;
+    AcceptPlan pl;
+    st = make_plan(B, N, V, flags & TV_ACCEPT_GREEDY, pl);
+    if (st != TV_OK) return st;
+    if (workspace_bytes < pl.total) return TV_ERR_WORKSPACE;
+    return launch_accept(q_logits, p_logits, draft_tokens, parent, seq_nodes, B, N, V, philox_seed, temperature, flags,
+                         accept_len, accepted_nodes, out_tokens, static_cast<char*>(workspace), pl,
+                         (hipStream_t)stream);
+}
+
 extern "C" int tv_spec_accept(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
                               const int32_t* parent, int B, int N, int V, uint64_t philox_seed, float temperature,
                               int greedy, int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
                               void* workspace, size_t workspace_bytes, void* stream) {
-    using namespace tv;
-    if (B < 0 || N < 1 || V < 1) return TV_ERR_INVALID_ARG;
-    if (N > TV_MAX_NODES) return TV_ERR_UNSUPPORTED;
-    if (!greedy && !(temperature > 0.f && temperature <= FLT_MAX)) return TV_ERR_INVALID_ARG;
-    if (B == 0) return TV_OK;
-    if (!q_logits || (!greedy && !p_logits) || !draft_tokens || !parent || !accept_len || !accepted_nodes ||
-        !out_tokens)
-        return TV_ERR_INVALID_ARG;
-    if (!aligned(q_logits, 4) || (!greedy && !aligned(p_logits, 4))) return TV_ERR_INVALID_ARG;
-    if (!workspace || !aligned(workspace, 256)) return TV_ERR_WORKSPACE;
-    AcceptPlan pl;
-    const int st = make_plan(B, N, V, greedy, pl);
-    if (st != TV_OK) return st;
-    if (workspace_bytes < pl.total) return TV_ERR_WORKSPACE;
-
-    char* ws = static_cast<char*>(workspace);
-    AccArgs a;
-    a.q = q_logits;
-    a.p = p_logits;
-    a.draft = draft_tokens;
-    a.parent = parent;
-    a.accept_len = accept_len;
-    a.accepted = accepted_nodes;
-    a.tokens = out_tokens;
-    a.ctrl = reinterpret_cast<uint64_t*>(ws + pl.ctrl_off);
-    a.stats = reinterpret_cast<uint64_t*>(ws + pl.stats_off);
-    a.mass = greedy ? nullptr : reinterpret_cast<double*>(ws + pl.mass_off);
-    a.B = B;
-    a.N = N;
-    a.V = V;
-    a.W = pl.W;
-    a.slice = pl.slice;
-    a.nteams = pl.nteams;
-    a.c = greedy ? 1.f : (float)(1.4426950408889634 / (double)temperature);
-    a.inv_t64 = greedy ? 1.0 : 1.0 / (double)temperature;
-    a.seed = philox_seed;
-    const bool vec4 = (V % 4 == 0) && aligned(q_logits, 16) && (greedy || aligned(p_logits, 16));
-    // The grid never exceeds the resident capacity from the occupancy query, so
-    // once earlier work on the stream drains every member is resident and the
-    // polls for other members' words make progress (their spins are bounded
-    // regardless).
-    hipLaunchKernelGGL(pick(greedy, vec4), dim3(pl.nteams * pl.W), dim3(kThreads), 0, (hipStream_t)stream, a);
-    return launch_status();
+    return tv_spec_accept_ex(q_logits, p_logits, draft_tokens, parent, nullptr, B, N, V, philox_seed, temperature,
+                             greedy ? TV_ACCEPT_GREEDY : 0, accept_len, accepted_nodes, out_tokens, workspace,
+                             workspace_bytes, stream);
 }
 
 extern "C" int tv_philox_uniforms(uint64_t seed, const uint32_t* triples, int n, float* out_u, uint32_t* out_raw,

@@ -36,9 +36,13 @@
 //    than 2^8), so most tiles skip the accumulator rescale; masks are applied
 //    only on tree tiles and the ragged last tile.  The exponentials of one row
 //    block are scheduled between the MFMAs of the other.
-//  * Tree keys are one or two extra tiles processed by the last KV split; the
-//    mask bit for (row, key j) is bit j of the row's 64-bit ancestor word,
-//    held in a register.
+//  * Tree keys are extra tiles processed by the last KV split; the mask bit for
+//    (row, key j) is bit j % 64 of the row's ancestor word j / 64 (the first
+//    word is held in a register, later ones are loaded by the tree tiles that
+//    need them).
+//  * Ragged batches: a sequence's own node count bounds its query rows, its own
+//    cache length bounds its key tiles; splits past a short cache publish an
+//    empty partial.
 //  * Long caches are split across workgroups; each writes its partial
 //    (max, sum, unnormalised O) with device-scope stores, and the last one to
 //    finish (device-scope counter) merges them and writes the output.
@@ -67,12 +71,14 @@ struct AttnArgs {
     const uint16_t* Vc;
     const uint16_t* Kt;
     const uint16_t* Vt;
-    const uint64_t* anc;
+    const uint64_t* anc;        // [B][N][W]
+    const int32_t* seq_nodes;   // [B] or null
+    const int32_t* seq_len;     // [B] or null
     float* out;
     float* part_o;     // [groups][nsplit][rows per tile][HD]
     float* part_ml;    // [groups][nsplit][rows per tile][2]
     uint32_t* counter; // [groups], zero between calls
-    int N, Hq, Hkv, G, L, R;
+    int N, Hq, Hkv, G, L, R, W;
     int row_tiles, nsplit, tiles_per_split, cache_tiles, tree_tiles, nblocks;
     float scale_log2;
 };
@@ -140,6 +146,19 @@ WsLayout workspace_layout(int B, int Hkv, const Plan& p) {
     w.part_ml_off = w.part_o_off + round_up(rows * HD * sizeof(float), 256);
     w.total = w.part_ml_off + round_up(rows * 2 * sizeof(float), 256);
     return w;
+}
+
+// Nodes and committed cache length of sequence b (ragged batches), clamped
+// into 0..N and 0..L.
+__device__ __forceinline__ int seq_nodes_of(const AttnArgs& a, int b) {
+    return a.seq_nodes ? min(max(a.seq_nodes[b], 0), a.N) : a.N;
+}
+__device__ __forceinline__ int seq_len_of(const AttnArgs& a, int b) {
+    return a.seq_len ? min(max(a.seq_len[b], 0), a.L) : a.L;
+}
+// Ancestor word w of node `node` of sequence b.
+__device__ __forceinline__ uint64_t anc_word(const AttnArgs& a, int b, int node, int w) {
+    return a.anc[((size_t)b * a.N + node) * a.W + w];
 }
 
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
@@ -210,11 +229,19 @@ __device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
 }
 
 
-// bf16 bits -> fp16, two values per dword (exact for normal fp16 magnitudes).
+// Two floats to fp16 rounded toward zero (v_cvt_pkrtz_f16_f32).  V values
+// come from bf16, whose 8-bit significands fp16 holds exactly over its normal
+// range, so the rounding mode matters only there: beyond +-65504 rounding
+// toward zero gives +-65504 (a saturating conversion, where rounding to
+// nearest would give infinities that turn whole output rows into NaN), and
+// below the normal range it truncates instead of rounding (< 6e-8).
+__device__ __forceinline__ uint32_t f32x2_to_f16x2_sat(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// bf16 bits -> fp16, two values per dword, saturated.
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-    const float a = __uint_as_float(w << 16), b = __uint_as_float(w & 0xffff0000u);
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+    return f32x2_to_f16x2_sat(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
 // Max over the two halves of the wave (lanes l and l ^ 32 hold one query row).
@@ -327,15 +354,22 @@ __device__ void merge_partials(const AttnArgs& a, char* lds, int grp, int row0, 
 template <int NT, int ROWS>
 __device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp, int row0, int nrows, int b,
                              int g) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have landed
+    // every wave releases its partial stores at agent scope, the barrier orders
+    // them before the arrival; the last workgroup acquires before it reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev =
-            __hip_atomic_fetch_add(&a.counter[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&a.counter[grp], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = prev == (uint32_t)a.nsplit - 1;
     }
     __syncthreads();
     if (!*s_flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (nrows <= 0) {  // a row tile of padding nodes only (ragged batch): nothing to merge
+        if (threadIdx.x == 0) __hip_atomic_store(&a.counter[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
 
     // last workgroup of the group.  Up to four splits: 32 loads in flight per
     // thread (16 in the 512-thread kernel, whose register budget is half as
@@ -387,16 +421,18 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
     const int b = bg / a.Hkv;
     const int g = bg % a.Hkv;
     const float c = a.scale_log2;
+    const int Rb = a.G * seq_nodes_of(a, b);  // this sequence's query rows
+    const int lb = seq_len_of(a, b);          // and its committed cache entries
 
     // ---- the query rows this lane carries as B-operand columns ----
     int row[RBW];
     bool row_ok[RBW];
     bf16x8 qf[RBW][8];
-    uint64_t anc_row[RBW];
+    uint64_t anc_row[RBW];  // ancestor word 0
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
         row[j] = rt * ROWS + rw * WROWS + 32 * j + n;
-        row_ok[j] = row[j] < a.R;
+        row_ok[j] = row[j] < Rb;
         const int node = row_ok[j] ? row[j] / a.G : 0;
         const int head = g * a.G + (row_ok[j] ? row[j] % a.G : 0);
         const uint16_t* qrow = a.Q + ((size_t)(b * a.N + node) * a.Hq + head) * HD;
@@ -405,12 +441,12 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
             const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
             qf[j][s] = __builtin_bit_cast(bf16x8, row_ok[j] ? v : u32x4{0, 0, 0, 0});
         }
-        anc_row[j] = row_ok[j] ? a.anc[(size_t)b * a.N + node] : 0ull;
+        anc_row[j] = row_ok[j] ? anc_word(a, b, node, 0) : 0ull;
     }
 
     // ---- tiles of this workgroup: cache tiles of the split, then tree tiles ----
     const int t_begin = split * a.tiles_per_split;
-    int n_cache = a.cache_tiles - t_begin;
+    int n_cache = (lb + KT - 1) / KT - t_begin;
     if (n_cache > a.tiles_per_split) n_cache = a.tiles_per_split;
     if (n_cache < 0) n_cache = 0;
     const int n_tree = (split == a.nsplit - 1) ? a.tree_tiles : 0;
@@ -430,7 +466,7 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
         size_t stride;
         if (!is_tree) {
             key0 = (t_begin + k_idx) * KT;
-            nk = min(KT, a.L - key0);
+            nk = min(KT, lb - key0);
             const size_t base = ((size_t)bg * a.L + key0) * HD;
             ks = a.Kc + base;
             vs = a.Vc + base;
@@ -506,7 +542,7 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
         if (k_idx >= n_tiles) continue;  // uniform per wave
         const bool is_tree = k_idx >= n_cache;
         const int key0 = is_tree ? (k_idx - n_cache) * KT : (t_begin + k_idx) * KT;
-        const int nk = is_tree ? min(KT, a.N - key0) : min(KT, a.L - key0);
+        const int nk = is_tree ? min(KT, a.N - key0) : min(KT, lb - key0);
         const bool masked = is_tree || nk < KT;
 
         // LDS byte addresses.  Rows are 256-byte aligned, so a chunk index can
@@ -557,7 +593,12 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
 #pragma unroll
                 for (int j = 0; j < RBW; ++j) {
                     uint32_t vis = ragged;
-                    if (is_tree) vis &= (uint32_t)(anc_row[j] >> ((key0 + kbase) & 63));
+                    if (is_tree) {
+                        const int word = (key0 + kbase) >> 6;  // uniform
+                        const uint64_t aw = word == 0 ? anc_row[j]
+                                                      : (row_ok[j] ? anc_word(a, b, row[j] / a.G, word) : 0ull);
+                        vis &= (uint32_t)(aw >> ((key0 + kbase) & 63));
+                    }
                     vis >>= 4 * hf;
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
@@ -646,7 +687,7 @@ __global__ __launch_bounds__(64 * NW) void tree_attention_kernel(const AttnArgs 
     //  merged path below gathers rows instead.
     const int grp = bg * a.row_tiles + rt;
     const int row0 = rt * ROWS;
-    const int nrows = min(ROWS, a.R - row0);
+    const int nrows = min(ROWS, Rb - row0);
 
     if constexpr (KG == 1) {
         if (a.nsplit == 1) {
@@ -815,11 +856,14 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     const int g = bg % a.Hkv;
     const float c = a.scale_log2;
 
+    const int Rb = a.G * seq_nodes_of(a, b);  // this sequence's query rows
+    const int lb = seq_len_of(a, b);          // and its committed cache entries
+
     // ---- the query row this lane carries as a B-operand column ----
     const int row = rt * ROWS + wave * 32 + n;
-    const bool row_ok = row < a.R;
+    const bool row_ok = row < Rb;
     bf16x8 qf[8];
-    uint64_t anc_row;
+    uint64_t anc_row;  // ancestor word 0
     {
         const int node = row_ok ? row / a.G : 0;
         const int head = g * a.G + (row_ok ? row % a.G : 0);
@@ -829,12 +873,12 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
             const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hf);
             qf[s] = __builtin_bit_cast(bf16x8, row_ok ? v : u32x4{0, 0, 0, 0});
         }
-        anc_row = row_ok ? a.anc[(size_t)b * a.N + node] : 0ull;
+        anc_row = row_ok ? anc_word(a, b, node, 0) : 0ull;
     }
 
     // ---- tiles of this workgroup: cache tiles of the split, then tree tiles ----
     const int t_begin = split * a.tiles_per_split;
-    int n_cache = a.cache_tiles - t_begin;
+    int n_cache = (lb + KT - 1) / KT - t_begin;
     if (n_cache > a.tiles_per_split) n_cache = a.tiles_per_split;
     if (n_cache < 0) n_cache = 0;
     const int nt = n_cache + ((split == a.nsplit - 1) ? a.tree_tiles : 0);
@@ -864,7 +908,7 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         const char* ks = reinterpret_cast<const char*>((tree ? a.Kt : a.Kc) + base);
         const char* vs = reinterpret_cast<const char*>((tree ? a.Vt : a.Vc) + base);
         const uint32_t stride = tree ? (uint32_t)a.Hkv * kRowBytes : (uint32_t)kRowBytes;
-        const int nk = min(KT, (tree ? a.N : a.L) - key0);
+        const int nk = min(KT, (tree ? a.N : lb) - key0);
         const uint32_t dst = stage(u) + r0 * kRowBytes;
         if (!tree && nk == KT) {  // uniform: a full cache tile
 #pragma unroll
@@ -912,7 +956,7 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t x = e < 2 ? part[hh][0][e] : part[hh][1][e - 2];
-                w[e] = pack_f16(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
+                w[e] = f32x2_to_f16x2_sat(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
             }
             *(lds_u32x4*)(uintptr_t)(sb + TILE + (r0 + 8 * hh) * kRowBytes + lane * 16) = w;
         }
@@ -964,10 +1008,14 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         // so block kb of it is word kb of the row's ancestor bits.
         if (masked) {  // uniform
             const bool is_tree = t >= n_cache;
-            const int nk = is_tree ? a.N : min(KT, a.L - (t_begin + t) * KT);
+            const int tt = t - n_cache;  // tree tile: keys 64 tt .., ancestor word tt
+            const int nk = is_tree ? min(KT, a.N - KT * tt) : min(KT, lb - (t_begin + t) * KT);
             const int kbase = 32 * kb;
             uint32_t vis = nk - kbase >= 32 ? 0xffffffffu : (nk - kbase <= 0 ? 0u : (1u << (nk - kbase)) - 1u);
-            if (is_tree) vis &= (uint32_t)(anc_row >> kbase);
+            if (is_tree) {
+                const uint64_t aw = tt == 0 ? anc_row : (row_ok ? anc_word(a, b, row / a.G, tt) : 0ull);
+                vis &= (uint32_t)(aw >> kbase);
+            }
             vis >>= 4 * hf;
 #pragma unroll
             for (int e = 0; e < 16; ++e)
@@ -1036,51 +1084,55 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         s_cur = s_next;
     };
 
-    // ---- prologue: DMA of tiles 0-2; tiles 0 and 1 converted; S(0); K(1)
-    // in registers; P(-1) = 0 with finite V(-1) ----
+    // a split past a short cache (ragged batch) has no tiles: it publishes an
+    // empty partial (m = -inf, l = 0, O = 0) and joins the merge
+    if (nt > 0) {
+        // ---- prologue: DMA of tiles 0-2; tiles 0 and 1 converted; S(0); K(1)
+        // in registers; P(-1) = 0 with finite V(-1) ----
 #pragma unroll
-    for (int u = 0; u < 3; ++u) issue_dma(u);
-    wait_vmcnt<4>();  // tiles 0 and 1 have landed
-    convert(0);
-    convert(1);
-    __syncthreads();  // tiles 0 and 1 are visible
-    read_k(ring_addr, 0);
-    {
-        f32x16 acc = f32x16{};
+        for (int u = 0; u < 3; ++u) issue_dma(u);
+        wait_vmcnt<4>();  // tiles 0 and 1 have landed
+        convert(0);
+        convert(1);
+        __syncthreads();  // tiles 0 and 1 are visible
+        read_k(ring_addr, 0);
+        {
+            f32x16 acc = f32x16{};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
-        s_cur = acc;
-    }
-    read_k(ring_addr, 1);
-    pf[0] = pf[1] = u32x4{0, 0, 0, 0};
+            for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], acc, 0, 0, 0);
+            s_cur = acc;
+        }
+        read_k(ring_addr, 1);
+        pf[0] = pf[1] = u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) vf[h][blk] = u32x4{0, 0, 0, 0};
+            for (int blk = 0; blk < 4; ++blk) vf[h][blk] = u32x4{0, 0, 0, 0};
 
-    const int n_full = (t_begin + n_cache) * KT <= a.L ? n_cache : n_cache - 1;
-    for (int t = 0; t < nt; ++t) {
-        const bool masked = t >= n_full;  // tree tiles and a ragged last cache tile
-        issue_dma(t + 3);
-        block(masked, t, 0);
-        block(masked, t, 1);
-        wait_vmcnt<4>();  // tile t+2 has landed (tile t+3 still in flight)
-        convert(t + 2);
-        __syncthreads();  // tile t+2 is visible; tile t-1's last reads are consumed
-    }
-    // the last block's P.V
+        const int n_full = (t_begin + n_cache) * KT <= lb ? n_cache : n_cache - 1;
+        for (int t = 0; t < nt; ++t) {
+            const bool masked = t >= n_full;  // tree tiles and a ragged last cache tile
+            issue_dma(t + 3);
+            block(masked, t, 0);
+            block(masked, t, 1);
+            wait_vmcnt<4>();  // tile t+2 has landed (tile t+3 still in flight)
+            convert(t + 2);
+            __syncthreads();  // tile t+2 is visible; tile t-1's last reads are consumed
+        }
+        // the last block's P.V
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-        o_acc[s & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf[s >> 2][s & 3]),
-                                                              __builtin_bit_cast(f16x8, pf[s >> 2]), o_acc[s & 3], 0,
-                                                              0, 0);
-    wait_vmcnt<0>();  // no copy into this workgroup's LDS outlives it
+        for (int s = 0; s < 8; ++s)
+            o_acc[s & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf[s >> 2][s & 3]),
+                                                                  __builtin_bit_cast(f16x8, pf[s >> 2]), o_acc[s & 3], 0,
+                                                                  0, 0);
+        wait_vmcnt<0>();  // no copy into this workgroup's LDS outlives it
+    }
 
     const float l_tot = halves_sum(l_run);
     const float m_log = (m_used == -INFINITY) ? -INFINITY : m_used * c;  // log2 units from here on
     const int grp = bg * a.row_tiles + rt;
     const int row0 = rt * ROWS;
-    const int nrows = min(ROWS, a.R - row0);
+    const int nrows = min(ROWS, Rb - row0);
 
     if (a.nsplit == 1) {
         if (row_ok) {
@@ -1126,10 +1178,11 @@ extern "C" size_t tv_tree_attention_workspace(int B, int N, int Hq, int Hkv, int
     return tv::workspace_layout(B, Hkv, p).total;
 }
 
-extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t* V_cache,
-                                 const uint16_t* K_tree, const uint16_t* V_tree, const uint64_t* anc_mask,
-                                 float* out, int B, int N, int Hq, int Hkv, int D, int L, float scale,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" int tv_tree_attention_ex(const uint16_t* Q, const uint16_t* K_cache, const uint16_t* V_cache,
+                                    const uint16_t* K_tree, const uint16_t* V_tree, const uint64_t* anc_mask,
+                                    float* out, const int32_t* seq_nodes, const int32_t* seq_len, int B, int N,
+                                    int Hq, int Hkv, int D, int L, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
     using namespace tv;
     if (B < 0 || N < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || L < 0) return TV_ERR_INVALID_ARG;
     if (N > TV_MAX_NODES || D != TV_HEAD_DIM) return TV_ERR_UNSUPPORTED;
@@ -1138,7 +1191,8 @@ extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, con
     if (!Q || !K_tree || !V_tree || !anc_mask || !out) return TV_ERR_INVALID_ARG;
     if (L > 0 && (!K_cache || !V_cache)) return TV_ERR_INVALID_ARG;
     if (!aligned(Q, 16) || !aligned(K_tree, 16) || !aligned(V_tree, 16) || !aligned(out, 16) ||
-        !aligned(anc_mask, 8) || (L > 0 && (!aligned(K_cache, 16) || !aligned(V_cache, 16))))
+        !aligned(anc_mask, 8) || (L > 0 && (!aligned(K_cache, 16) || !aligned(V_cache, 16))) ||
+        (seq_nodes && !aligned(seq_nodes, 4)) || (seq_len && !aligned(seq_len, 4)))
         return TV_ERR_INVALID_ARG;
     const long rows = (long)B * Hkv * (Hq / Hkv) * N;
     if ((long)B * N * Hq > (1L << 30) || rows > (1L << 30)) return TV_ERR_UNSUPPORTED;
@@ -1154,6 +1208,8 @@ extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, con
     a.Kt = K_tree;
     a.Vt = V_tree;
     a.anc = anc_mask;
+    a.seq_nodes = seq_nodes;
+    a.seq_len = seq_len;
     a.out = out;
     char* ws = static_cast<char*>(workspace);
     a.counter = wl.total ? reinterpret_cast<uint32_t*>(ws + wl.counter_off) : nullptr;
@@ -1165,6 +1221,7 @@ extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, con
     a.G = Hq / Hkv;
     a.L = L;
     a.R = p.R;
+    a.W = TV_MASK_WORDS(N);
     a.row_tiles = p.row_tiles;
     a.nsplit = p.nsplit;
     a.tiles_per_split = p.tiles_per_split;
@@ -1191,4 +1248,12 @@ extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, con
             break;
     }
     return launch_status();
+}
+
+extern "C" int tv_tree_attention(const uint16_t* Q, const uint16_t* K_cache, const uint16_t* V_cache,
+                                 const uint16_t* K_tree, const uint16_t* V_tree, const uint64_t* anc_mask,
+                                 float* out, int B, int N, int Hq, int Hkv, int D, int L, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    return tv_tree_attention_ex(Q, K_cache, V_cache, K_tree, V_tree, anc_mask, out, nullptr, nullptr, B, N, Hq, Hkv,
+                                D, L, scale, workspace, workspace_bytes, stream);
 }

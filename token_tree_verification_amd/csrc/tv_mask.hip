@@ -9,35 +9,48 @@
 namespace tv {
 namespace {
 
-// One workgroup of 64 lanes per sequence, one lane per node (N <= 64).
-__global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict__ parent, int N,
-                                                        uint64_t* __restrict__ anc, int32_t* __restrict__ depth,
-                                                        int32_t* __restrict__ seq_status) {
+constexpr int kMaskWords = TV_MASK_WORDS(TV_MAX_NODES);
+
+// One workgroup per sequence, one lane per node (up to TV_MAX_NODES lanes).
+// Node i chases parent pointers (held in LDS) up to the root, setting one bit
+// per node on the way; parent[j] < j makes every chase end within i steps.
+__global__ __launch_bounds__(TV_MAX_NODES) void tree_mask_kernel(const int32_t* __restrict__ parent,
+                                                                  const int32_t* __restrict__ seq_nodes, int N,
+                                                                  uint64_t* __restrict__ anc, int32_t* __restrict__ depth,
+                                                                  int32_t* __restrict__ seq_status) {
     const int b = blockIdx.x;
     const int i = threadIdx.x;
+    const int W = TV_MASK_WORDS(N);
     const int32_t* par = parent + (size_t)b * N;
+    const int nb = seq_nodes ? seq_nodes[b] : N;
     __shared__ int32_t sp[TV_MAX_NODES];
-    int ok = 1;
-    if (i < N) {
+    int ok = nb >= 1 && nb <= N;
+    if (ok && i < nb) {
         const int p = par[i];
         sp[i] = p;
         ok = (i == 0) ? (p == -1) : (p >= 0 && p < i);
     }
-    // every lane of the single wave votes; any invalid node invalidates the sequence
-    const bool all_ok = __all(ok);
-    __syncthreads();
+    // any invalid node invalidates the sequence (the barrier also publishes sp)
+    const bool all_ok = __syncthreads_and(ok) != 0;
     if (i < N) {
-        uint64_t bits = 0;
+        uint64_t bits[kMaskWords] = {};
         int d = -1;
-        if (all_ok) {
-            // parent[j] < j guarantees the chase ends at the root within i steps
+        if (all_ok && i < nb) {
             for (int j = i; j != -1; j = sp[j]) {
-                bits |= 1ull << j;
+#pragma unroll
+                for (int w = 0; w < kMaskWords; ++w)
+                    if (w == (j >> 6)) bits[w] |= 1ull << (j & 63);
                 ++d;
             }
         }
-        anc[(size_t)b * N + i] = all_ok ? bits : 0ull;
-        depth[(size_t)b * N + i] = all_ok ? d : -1;
+        for (int w = 0; w < W; ++w) {
+            uint64_t v = 0;
+#pragma unroll
+            for (int k = 0; k < kMaskWords; ++k)
+                if (k == w) v = bits[k];
+            anc[((size_t)b * N + i) * W + w] = v;
+        }
+        depth[(size_t)b * N + i] = d;
     }
     if (i == 0 && seq_status) seq_status[b] = all_ok ? TV_OK : TV_ERR_BAD_TREE;
 }
@@ -45,14 +58,22 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict
 }  // namespace
 }  // namespace tv
 
-extern "C" int tv_build_tree_mask(const int32_t* parent, int B, int N, uint64_t* anc_mask, int32_t* depth,
-                                  int32_t* seq_status, void* stream) {
+extern "C" int tv_build_tree_mask_ex(const int32_t* parent, const int32_t* seq_nodes, int B, int N,
+                                     uint64_t* anc_mask, int32_t* depth, int32_t* seq_status, void* stream) {
     if (B < 0 || N < 1) return TV_ERR_INVALID_ARG;
     if (N > TV_MAX_NODES) return TV_ERR_UNSUPPORTED;
     if (B == 0) return TV_OK;
     if (!parent || !anc_mask || !depth) return TV_ERR_INVALID_ARG;
-    if (!tv::aligned(anc_mask, 8) || !tv::aligned(parent, 4) || !tv::aligned(depth, 4)) return TV_ERR_INVALID_ARG;
-    hipLaunchKernelGGL(tv::tree_mask_kernel, dim3(B), dim3(64), 0, (hipStream_t)stream, parent, N, anc_mask, depth,
-                       seq_status);
+    if (!tv::aligned(anc_mask, 8) || !tv::aligned(parent, 4) || !tv::aligned(depth, 4) ||
+        (seq_nodes && !tv::aligned(seq_nodes, 4)))
+        return TV_ERR_INVALID_ARG;
+    const int threads = (N + 63) / 64 * 64;
+    hipLaunchKernelGGL(tv::tree_mask_kernel, dim3(B), dim3(threads), 0, (hipStream_t)stream, parent, seq_nodes, N,
+                       anc_mask, depth, seq_status);
     return tv::launch_status();
+}
+
+extern "C" int tv_build_tree_mask(const int32_t* parent, int B, int N, uint64_t* anc_mask, int32_t* depth,
+                                  int32_t* seq_status, void* stream) {
+    return tv_build_tree_mask_ex(parent, nullptr, B, N, anc_mask, depth, seq_status, stream);
 }
