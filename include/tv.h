@@ -51,7 +51,8 @@ typedef enum {
     TV_ERR_UNSUPPORTED = -2, /* valid but not implemented here: N > TV_MAX_NODES, D != 128 */
     TV_ERR_BAD_TREE = -3,    /* parent[] violates the tree conventions (per-sequence status) */
     TV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the query says */
-    TV_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+    TV_ERR_HIP = -5,         /* a HIP launch or runtime call failed */
+    TV_ERR_SCRATCH = -6      /* the shape needs more than TV_NOALLOC_SCRATCH_BYTES (allocation-free call) */
 } tv_status;
 
 /* Largest tree (nodes including the root) handled. */
@@ -228,6 +229,27 @@ int tv_spec_accept_ex(const float* q_logits, const float* p_logits, const int32_
  * team (each owns one vocabulary slice of every row), teams, and the slice
  * length.  Any output pointer may be NULL.  Host only. */
 int tv_spec_accept_plan(int B, int N, int V, int greedy, int* team_size, int* teams, int* slice);
+
+/*
+ * tv_spec_accept_noalloc -- tv_spec_accept_ex without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Its scratch is a static device array of
+ * TV_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, held until the process ends; it
+ * covers every plan of trees up to 64 nodes, and of larger trees with few
+ * enough sequences (256-node trees in sampling mode with 256 sequences need
+ * 6.1 MiB and are refused); the first
+ * call on a device zeroes its control words with a small kernel on `stream`.
+ * Shapes whose plan (tv_spec_accept_workspace) needs more return
+ * TV_ERR_SCRATCH before anything is enqueued.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ */
+#define TV_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int tv_spec_accept_noalloc(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
+                           const int32_t* parent, const int32_t* seq_nodes, int B, int N, int V,
+                           uint64_t philox_seed, float temperature, int flags, int32_t* accept_len,
+                           int32_t* accepted_nodes, int32_t* out_tokens, void* stream);
 
 /* For tests and diagnostics: the number of polls each team wait of later
  * accept calls makes before it gives up (process-wide).  0 makes every wait

@@ -139,17 +139,21 @@ __device__ __forceinline__ void wait_failed(uint64_t* line, uint64_t* done) {
     asm volatile("" : : "v"(old));
 }
 
-// Walk steps exchange tagged words: the tag is (generation << 12 | sequence
-// iteration mod 16 << 8 | rejection pass) in the upper 32 bits of every 64-bit
-// word.  A slot is indexed by the pass, and the members of a team are never
-// more than one sequence apart during a walk (each needs every member's
-// statistics of its sequence first), so a word from an earlier sequence or
-// call is told apart (an older call would have to be 2^20 calls back).
-// Statistics entries use (generation << 12 | sequence of the team) the same
-// way.
+// Walk steps exchange tagged words: the tag is (1 << 31 | generation mod 2^19
+// << 12 | sequence iteration mod 16 << 8 | rejection pass) in the upper 32
+// bits of every 64-bit word.  A slot is indexed by the pass, and the members
+// of a team are never more than one sequence apart during a walk (each needs
+// every member's statistics of its sequence first), so a word from an earlier
+// sequence or call is told apart (an older call would have to be 2^19 calls
+// back), and the top bit keeps every tag apart from never-written (zero)
+// memory.  Statistics entries use (1 << 31 | generation << 12 | sequence of
+// the team) the same way.
+__device__ __forceinline__ uint32_t gen_tag(const TeamSync& s) {
+    return 0x80000000u | (((uint32_t)(s.base >> kTagShift) & 0x7ffffu) << 12);
+}
 __device__ __forceinline__ uint32_t exchange_tag(const TeamSync& s, int iter, int pass) {
     static_assert(kMaxNodes <= 257, "rejection passes of one walk fit eight bits");
-    return (uint32_t)(((s.base >> kTagShift) << 12) | ((uint32_t)(iter & 15) << 8) | (uint32_t)(pass & 255));
+    return gen_tag(s) | ((uint32_t)(iter & 15) << 8) | (uint32_t)(pass & 255);
 }
 // Poll one member's first nw words until all carry tag `tg` (upper half); at
 // most s.limit polls (none when the limit is 0).
@@ -825,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)s_base);
             have_base = true;
         }
-        const uint64_t stag = (uint64_t)(uint32_t)(((sync.base >> kTagShift) << 12) | ((uint32_t)iter & 0xfffu)) << 32;
+        const uint64_t stag = (uint64_t)(gen_tag(sync) | ((uint32_t)iter & 0xfffu)) << 32;
         uint64_t* stats = a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)2 * (GREEDY ? N : 2 * N) * W;
         stream_slices<GREEDY, VEC4>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag, s_srow);
         if constexpr (GREEDY) {
@@ -1317,6 +1321,65 @@ extern "C" int tv_spec_accept_ex(const float* q_logits, const float* p_logits, c
     return launch_accept(q_logits, p_logits, draft_tokens, parent, seq_nodes, B, N, V, philox_seed, temperature, flags,
                          accept_len, accepted_nodes, out_tokens, static_cast<char*>(workspace), pl,
                          (hipStream_t)stream);
+}
+
+namespace tv {
+namespace {
+
+// ---------------------------------------------- the allocation-free variant --
+// Scratch of tv_spec_accept_noalloc: file-scope device memory, one copy per
+// GPU (held until the process ends).  Host code never passes `scratch` itself
+// to a kernel (in host code it is only a stand-in for the symbol): it uses the
+// device address that hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = TV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+// The scratch's device address on the current device, with its control lines
+// (team generations, wait marks, arrival word) zeroed once, on `stream`,
+// before first use.  Every other word the kernel reads carries a nonzero tag,
+// so never-written scratch is never taken for data.  nullptr on failure.
+char* device_scratch(hipStream_t stream) {
+    static std::mutex mu;
+    static char* ptr[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        const size_t ctrl = (size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t);
+        const size_t n16 = (round_up(ctrl, 256) + 256) / 16;  // control lines and the arrival word
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint4*>(p), n16);
+        if (hipGetLastError() != hipSuccess) return nullptr;
+        ptr[dev] = static_cast<char*>(p);
+    }
+    return ptr[dev];
+}
+
+}  // namespace
+}  // namespace tv
+
+extern "C" int tv_spec_accept_noalloc(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
+                                      const int32_t* parent, const int32_t* seq_nodes, int B, int N, int V,
+                                      uint64_t philox_seed, float temperature, int flags, int32_t* accept_len,
+                                      int32_t* accepted_nodes, int32_t* out_tokens, void* stream) {
+    using namespace tv;
+    int st = check_accept_args(q_logits, p_logits, draft_tokens, parent, B, N, V, temperature, flags, accept_len,
+                               accepted_nodes, out_tokens);
+    if (st != TV_OK || B == 0) return st;
+    AcceptPlan pl;
+    st = make_plan(B, N, V, flags & TV_ACCEPT_GREEDY, pl);
+    if (st != TV_OK) return st;
+    if (pl.total > kScratchBytes) return TV_ERR_SCRATCH;
+    char* ws = device_scratch((hipStream_t)stream);
+    if (!ws) return TV_ERR_HIP;
+    return launch_accept(q_logits, p_logits, draft_tokens, parent, seq_nodes, B, N, V, philox_seed, temperature, flags,
+                         accept_len, accepted_nodes, out_tokens, ws, pl, (hipStream_t)stream);
 }
 
 extern "C" int tv_spec_accept(const float* q_logits, const float* p_logits, const int32_t* draft_tokens,
