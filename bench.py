@@ -431,6 +431,76 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
     return rec, first_inputs
 
 
+def measure_extras(args, tv, torch, dev, stream, lead_of):
+    """The steps around verification, on the headline workload's shapes: the
+    KV commit of the accepted paths, and one step of dynamic tree construction
+    (expanding ten frontier nodes per sequence with their top-10 tokens, then
+    the re-ranking of the 511-slot pool down to 64 nodes)."""
+    from workloads import CONFIGS, accept_inputs, attention_inputs
+    w = CONFIGS[args.config]
+    out = {}
+    # KV commit: the sampling walk's paths of this workload, appended after L
+    q, p, draft, parent = accept_inputs(w, device=dev)
+    a, nodes, _ = tv.spec_accept(q, p, draft, parent, seed=w.philox_seed, temperature=1.0)
+    del q, p
+    _, _, _, Kt, Vt = attention_inputs(w, device=dev, L=0)
+    Kc = torch.zeros((w.B, w.Hkv, w.L + w.N, w.D), dtype=torch.bfloat16, device=dev)
+    Vc = torch.zeros_like(Kc)
+    cl = torch.full((w.B,), w.L, dtype=torch.int32, device=dev)
+    nl = torch.empty_like(cl)
+    st = torch.empty_like(cl)
+    lib = tv.library()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    args_c = (P(Kt), P(Vt), P(a), P(nodes), P(cl), P(Kc), P(Vc), P(nl), P(st), w.B, w.N, w.Hkv, w.D, w.L + w.N, sp)
+
+    def commit(s):
+        rc = lib.tv_commit_kv(*args_c)
+        if rc:
+            raise RuntimeError(f"tv_commit_kv: {rc}")
+    ms = time_batch(commit, args.steps, stream, torch, lead_of(args.steps))
+    rows = int((a.clamp(min=-1) + 1).sum().item())
+    cbytes = rows * w.Hkv * w.D * 2 * 2 * 2  # K and V rows, read and written
+    out["commit_kv"] = {"us": round(ms * 1e3, 3), "rows": rows, "bytes": cbytes,
+                        "GB/s": round(cbytes / (ms / 1e3) / 1e9, 1)}
+    del Kc, Vc, Kt, Vt
+    # dynamic tree construction: one middle expansion step and the re-ranking
+    B, F, K, V = w.B, 10, 10, w.V
+    Pn = 1 + K + 5 * K * K
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    root_logits = torch.randn((B, 1, V), generator=g, device=dev) * 2.0
+    logits = torch.randn((B, F, V), generator=g, device=dev) * 2.0
+    pool = tv.tree_pool(B, Pn, dev)
+    frontier = tv.tree_expand(root_logits, None, pool, 1, K, F, 1.0)
+    nxt = torch.empty((B, F), dtype=torch.int32, device=dev)
+    args_e = (P(logits), P(frontier), None, B, F, V, K, ctypes.c_float(1.0), P(pool[0]), P(pool[1]), P(pool[2]), Pn,
+              1 + K, P(nxt), F, sp)
+
+    def expand(s):
+        rc = lib.tv_tree_expand(*args_e)
+        if rc:
+            raise RuntimeError(f"tv_tree_expand: {rc}")
+    ms = time_batch(expand, args.steps, stream, torch, lead_of(args.steps))
+    ebytes = B * F * V * 4
+    out["tree_expand"] = {"us": round(ms * 1e3, 3), "bytes": ebytes, "GB/s": round(ebytes / (ms / 1e3) / 1e9, 1),
+                          "hbm_frac": round(ebytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "shape": f"{B} sequences x {F} frontier rows x vocab {V}, top-{K}"}
+    outs = [torch.empty((B, w.N), dtype=torch.int32, device=dev) for _ in range(3)]
+    nn = torch.empty((B,), dtype=torch.int32, device=dev)
+    args_s = (P(pool[0]), P(pool[1]), P(pool[2]), B, Pn, 1 + K + F * K, w.N, *(P(o) for o in outs), P(nn), sp)
+
+    def select(s):
+        rc = lib.tv_tree_select(*args_s)
+        if rc:
+            raise RuntimeError(f"tv_tree_select: {rc}")
+    ms = time_batch(select, args.steps, stream, torch, lead_of(args.steps))
+    out["tree_select"] = {"us": round(ms * 1e3, 3), "shape": f"{B} pools of {1 + K + F * K} slots -> {w.N} nodes"}
+    del logits, root_logits, pool
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -455,6 +525,8 @@ def main():
     head, first_inputs = measure(args.config, args, tv, torch, dev, stream, lead, True)
     print(f"[bench] {args.config}: {head['ms_per_step'] * 1e3:.1f} us/step, calls_us {head['calls_us']}",
           file=sys.stderr, flush=True)
+    extras = measure_extras(args, tv, torch, dev, stream, lead)
+    print(f"[bench] around verification: {extras}", file=sys.stderr, flush=True)
     others = {}
     if not args.only:
         for name in [c.strip() for c in args.also.split(",") if c.strip()]:
@@ -491,6 +563,7 @@ def main():
         "accept": head["accept"],
         "greedy": head["greedy"],
         "achievable": peaks,
+        "around_verification": extras,
         "configs": others,
     }
     if not args.no_cpu_baseline:

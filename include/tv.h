@@ -260,6 +260,91 @@ int tv_spec_accept_noalloc(const float* q_logits, const float* p_logits, const i
 uint32_t tv_set_wait_limit(uint32_t polls);
 
 /*
+ * tv_commit_kv -- append the accepted path's keys and values to the cache.
+ *
+ * EAGLE explainer, implementation notes: verifying a tree needs KV memory
+ * beyond the committed context (the pass computes keys and values for every
+ * tree node); survey explainer, formal definition, accept/reject phase: the
+ * accepted drafts become output.  Sequence b with committed length
+ * cache_len[b] and accept_len[b] = a >= 0 appends a + 1 rows: the root (node 0,
+ * the last committed token, whose keys and values this pass computed) and
+ * accepted_nodes[b, 0..a-1] in path order, at positions cache_len[b] ..
+ * cache_len[b] + a, for every KV head.  The extra token drawn by the walk gets
+ * its keys and values in the next pass.
+ *
+ *   K_tree, V_tree   bf16 [B,N,Hkv,D]  keys and values of the tree nodes.
+ *   accept_len       int32 [B]         from tv_spec_accept (negative: failed walk).
+ *   accepted_nodes   int32 [B,N]       from tv_spec_accept.
+ *   cache_len        int32 [B]         committed lengths before the call.
+ *   K_cache, V_cache bf16 [B,Hkv,L,D]  updated in place (L = capacity per head).
+ *   new_cache_len    int32 [B]         out: cache_len + a + 1, or cache_len
+ *                                      when nothing is committed.  Must not
+ *                                      alias cache_len.
+ *   seq_status       int32 [B]         out, may be NULL: 0; TV_ERR_BAD_TREE when
+ *                                      a < 0 or the path names a node outside
+ *                                      1..N-1; TV_ERR_INVALID_ARG when the rows
+ *                                      do not fit (cache_len + a + 1 > L, or
+ *                                      a > N - 1).  Those sequences commit
+ *                                      nothing.
+ * The tree and cache buffers must not overlap.  Sizes: B >= 0,
+ * 1 <= N <= TV_MAX_NODES, Hkv >= 1, D == TV_HEAD_DIM, L >= 0.
+ */
+int tv_commit_kv(const uint16_t* K_tree, const uint16_t* V_tree, const int32_t* accept_len,
+                 const int32_t* accepted_nodes, const int32_t* cache_len, uint16_t* K_cache, uint16_t* V_cache,
+                 int32_t* new_cache_len, int32_t* seq_status, int B, int N, int Hkv, int D, int L,
+                 void* stream);
+
+/*
+ * tv_tree_expand / tv_tree_select -- dynamic draft-tree construction.
+ *
+ * EAGLE-3 explainer, integration with EAGLE-2 (the draft head plugs into
+ * EAGLE-2's dynamic tree generation at inference time), and the EAGLE
+ * explainer's conclusion (EAGLE-2 turns the static tree into a dynamic one).
+ * The pages give no steps; the construction taken is: a node's value is the
+ * draft's probability of its path from the root, kept as a cumulative log
+ * probability; each expansion gives every frontier node its top-k tokens as
+ * children and keeps the Fn most valuable new nodes as the next frontier; the
+ * final tree is the root plus the m - 1 most valuable nodes of the pool.
+ *
+ * A pool of P slots per sequence holds every node created: value (fp32),
+ * parent slot (-1: root or empty slot) and token.  Slot 0 is the root.
+ *
+ * tv_tree_expand: one expansion step.
+ *   draft_logits fp32 [B,F,V]  row f: the draft's logits at frontier node f.
+ *   frontier     int32 [B,F]   pool slots of the frontier (-1: empty), or NULL
+ *                              for the first step, which expands the root
+ *                              (F must be 1) and initialises slot 0 (value 0,
+ *                              parent -1, token root_token[b], or -1 when
+ *                              root_token is NULL).
+ *   topk         children per frontier node, 1..16: its topk largest logits
+ *                (ties to the smaller token id).  Child j of row f goes to
+ *                slot pool_base + f*topk + j, with value
+ *                fp32(value(parent) + log softmax(logits/T)[token]), the
+ *                log-softmax computed in fp64.  Rows of empty slots (and
+ *                children past V tokens) give empty slots (value -inf,
+ *                parent -1, token -1).
+ *   temperature  > 0 and finite.
+ *   next_frontier int32 [B,Fn]  out: the Fn best new slots by (value desc,
+ *                slot asc), -1 where fewer exist; may be NULL when Fn == 0.
+ *   Requires pool_base >= 1 and pool_base + F*topk <= P.
+ * tv_tree_select: the tree.  Keeps the root and the M - 1 best valid slots
+ * among 1..pool_count-1 (ties to the earlier slot; a child never outranks its
+ * parent, so the kept set is a tree), renumbered in slot order:
+ *   parent int32 [B,M]   out: parent node index (-1 for the root and padding).
+ *   tokens int32 [B,M]   out: tokens (slot 0's token for the root).
+ *   pool_index int32 [B,M] out: the pool slot of each node (-1 padding).
+ *   seq_nodes int32 [B]  out: nodes of each tree (a ragged batch when pools
+ *                        hold fewer than M - 1 valid slots).
+ *   Sizes: pool_count <= 4096, M <= TV_MAX_NODES.
+ */
+int tv_tree_expand(const float* draft_logits, const int32_t* frontier, const int32_t* root_token, int B, int F,
+                   int V, int topk, float temperature, float* pool_score, int32_t* pool_parent,
+                   int32_t* pool_token, int P, int pool_base, int32_t* next_frontier, int Fn, void* stream);
+int tv_tree_select(const float* pool_score, const int32_t* pool_parent, const int32_t* pool_token, int B, int P,
+                   int pool_count, int M, int32_t* parent, int32_t* tokens, int32_t* pool_index,
+                   int32_t* seq_nodes, void* stream);
+
+/*
  * tv_philox_uniforms -- the uniforms tv_spec_accept draws, for auditing.
  *
  *   triples  uint32 [n,3]  (node, sequence, purpose) counters, device memory.

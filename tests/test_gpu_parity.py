@@ -622,6 +622,117 @@ def test_accept_failed_waits_are_reported(tv):
             _compare_walk((_np(a), _np(n), _np(t)), ref, greedy)
 
 
+# ------------------------------------------------------------- KV commit --
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_commit_kv_bit_exact(tv, name):
+    """The paths the accept call chose on each workload (sampling and greedy),
+    appended to caches of committed lengths that differ per sequence: the
+    whole caches, new lengths and statuses bit-exact against the oracle."""
+    w = CONFIGS[name]
+    q, p, draft, parent_t = accept_inputs(w, device=dev())
+    T = [t for t in w.temperatures if t > 0][0]
+    rng = np.random.default_rng(3)
+    Lcap = 300 + w.N
+    _, _, _, Kt, Vt = attention_inputs(w, device=dev(), L=0)
+    for greedy in (False, True):
+        a, nodes, _ = tv.spec_accept(q, None if greedy else p, draft, parent_t, seed=2, temperature=T, greedy=greedy)
+        lens = rng.integers(0, 300, size=w.B).astype(np.int32)
+        lens[0] = Lcap - 1 - int(_np(a)[0])  # fills the cache exactly
+        Kc = torch.randn((w.B, w.Hkv, Lcap, 128), device=dev()).to(torch.bfloat16)
+        Vc = torch.randn((w.B, w.Hkv, Lcap, 128), device=dev()).to(torch.bfloat16)
+        host = [_np(x.view(torch.int16)) for x in (Kc, Vc, Kt, Vt)]
+        cl = torch.from_numpy(lens).to(dev())
+        new_len, st = tv.commit_kv(Kt, Vt, a, nodes, cl, Kc, Vc)
+        torch.cuda.synchronize()
+        K2, V2, nl, ost = oracle.commit_kv(host[0], host[1], host[2], host[3], _np(a), _np(nodes), lens)
+        assert np.array_equal(_np(st), ost) and (ost == 0).all()
+        assert np.array_equal(_np(new_len), nl)
+        assert np.array_equal(_np(Kc.view(torch.int16)), K2) and np.array_equal(_np(Vc.view(torch.int16)), V2)
+
+
+def test_commit_kv_edge_cases(tv):
+    """Failed walks, full caches and out-of-range node ids commit nothing and
+    say why; ragged lengths; the empty batch."""
+    B, N, Hkv, Lcap = 6, 9, 3, 20
+    Kt = torch.randn((B, N, Hkv, 128), device=dev()).to(torch.bfloat16)
+    Vt = torch.randn((B, N, Hkv, 128), device=dev()).to(torch.bfloat16)
+    Kc = torch.randn((B, Hkv, Lcap, 128), device=dev()).to(torch.bfloat16)
+    Vc = torch.randn((B, Hkv, Lcap, 128), device=dev()).to(torch.bfloat16)
+    acc = np.array([-1, -2, 3, 8, 2, 0], np.int32)
+    nodes = np.full((B, N), -1, np.int32)
+    nodes[2, :3] = [1, 4, 7]
+    nodes[3, :8] = np.arange(1, 9)
+    nodes[4, :2] = [3, 12]          # 12 is not a node
+    lens = np.array([0, 5, 17, 11, 0, 19], np.int32)  # sequence 2 does not fit (17 + 4 > 20)
+    host = [_np(x.view(torch.int16)) for x in (Kc, Vc, Kt, Vt)]
+    new_len, st = tv.commit_kv(Kt, Vt, torch.from_numpy(acc).to(dev()), torch.from_numpy(nodes).to(dev()),
+                               torch.from_numpy(lens).to(dev()), Kc, Vc)
+    torch.cuda.synchronize()
+    assert _np(st).tolist() == [-3, -3, -1, 0, -3, 0]
+    assert _np(new_len).tolist() == [0, 5, 17, 20, 0, 20]
+    K2, V2, nl, ost = oracle.commit_kv(host[0], host[1], host[2], host[3], acc, np.where(nodes > 8, 0, nodes), lens)
+    for b in (0, 1, 2, 4):  # nothing committed
+        assert np.array_equal(_np(Kc.view(torch.int16))[b], host[0][b])
+    for b in (3, 5):
+        assert np.array_equal(_np(Kc.view(torch.int16))[b], K2[b]) and np.array_equal(_np(Vc.view(torch.int16))[b], V2[b])
+    e = torch.zeros((0,), dtype=torch.int32, device=dev())
+    z = torch.zeros((0, N, Hkv, 128), dtype=torch.bfloat16, device=dev())
+    zc = torch.zeros((0, Hkv, Lcap, 128), dtype=torch.bfloat16, device=dev())
+    nl0, _ = tv.commit_kv(z, z, e, torch.zeros((0, N), dtype=torch.int32, device=dev()), e, zc, zc)
+    assert nl0.numel() == 0
+
+
+# ------------------------------------------------- dynamic tree construction --
+def _draft_rows(b_paths, V, seed):
+    """A synthetic draft model: a fixed random logit row per (sequence, path)."""
+    rows = []
+    for b, path in b_paths:
+        h = hash((seed, b, tuple(path))) % (2 ** 32)
+        rows.append(np.random.default_rng(h).normal(scale=2.0, size=V).astype(np.float32))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("B,V,topk,depth,M,T", [
+    (3, 1000, 4, 5, 40, 1.0),
+    (4, 128256, 10, 6, 60, 1.0),
+    (2, 32000, 1, 6, 7, 0.7),
+    (2, 10, 16, 3, 250, 1.3),   # topk past the vocabulary: empty slots, fewer nodes than M (ragged)
+])
+def test_dynamic_tree_bit_exact(tv, B, V, topk, depth, M, T):
+    """Every expansion step's pool values, parents, tokens and next frontier,
+    then the selected trees, bit-exact against the oracle; the trees then feed
+    the ragged tree mask."""
+    from oracle import dynamic_tree as dt
+    P = 1 + topk + (depth - 1) * topk * topk
+    pool = tv.tree_pool(B, P, dev())
+    o_score = np.full((B, P), -np.inf, np.float32)
+    o_par = np.full((B, P), -1, np.int32)
+    o_tok = np.full((B, P), -1, np.int32)
+    root = np.arange(B, dtype=np.int32) + 7
+    frontier, o_front, base = None, None, 1
+    for d in range(depth):
+        F = 1 if frontier is None else topk
+        slots = [[0] * F for _ in range(B)] if o_front is None else o_front.tolist()
+        paths = [(b, dt.path_tokens(o_par[b], o_tok[b], s) if s >= 0 else [-1]) for b in range(B) for s in slots[b]]
+        logits = _draft_rows(paths, V, 11).reshape(B, F, V)
+        frontier = tv.tree_expand(torch.from_numpy(logits).to(dev()), frontier, pool, base, topk, topk, T,
+                                  root_token=torch.from_numpy(root).to(dev()) if d == 0 else None)
+        o_front = dt.expand(logits, o_front, o_score, o_par, o_tok, base, topk, topk, T, root_token=root)
+        base += F * topk
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(pool[1]), o_par), f"parents differ after step {d}"
+        assert np.array_equal(_np(pool[2]), o_tok), f"tokens differ after step {d}"
+        assert np.array_equal(_np(pool[0]).view(np.uint32), o_score.view(np.uint32)), f"values differ after step {d}"
+        assert np.array_equal(_np(frontier), o_front), f"frontier differs after step {d}"
+    par, toks, idx, nodes = tv.tree_select(pool, base, M)
+    o_sel = dt.select(o_score, o_par, o_tok, base, M)
+    for got, want in zip((par, toks, idx, nodes), o_sel):
+        assert np.array_equal(_np(got), want)
+    anc, depth_t, st = tv.build_tree_mask(par, seq_nodes=nodes)
+    o_anc, o_depth, o_st = oracle.tree_mask(o_sel[0], seq_nodes=o_sel[3])
+    assert np.array_equal(_np(anc).view(np.uint64), o_anc) and (o_st == 0).all() and (_np(st) == 0).all()
+
+
 def test_graph_replay_matches_eager(tv):
     """The three calls captured in one HIP graph and replayed repeatedly, with
     eager work in between, give the eager results every time (the accept and

@@ -16,18 +16,26 @@ from ._binding import (  # noqa: F401
     accept_workspace_bytes,
     attention_workspace_bytes,
     build_tree_mask,
+    commit_kv,
     library,
     mask_words,
     philox_uniforms,
     set_wait_limit,
     spec_accept,
     tree_attention,
+    tree_expand,
+    tree_pool,
+    tree_select,
 )
 
 __all__ = [
     "build_tree_mask",
     "tree_attention",
     "spec_accept",
+    "commit_kv",
+    "tree_pool",
+    "tree_expand",
+    "tree_select",
     "accept_plan",
     "set_wait_limit",
     "mask_words",

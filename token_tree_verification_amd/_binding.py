@@ -62,6 +62,12 @@ def _load():
     lib.tv_spec_accept_plan.restype = I
     lib.tv_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.tv_set_wait_limit.restype = ctypes.c_uint32
+    lib.tv_commit_kv.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.tv_commit_kv.restype = I
+    lib.tv_tree_expand.argtypes = [P, P, P, I, I, I, I, F, P, P, P, I, I, P, I, P]
+    lib.tv_tree_expand.restype = I
+    lib.tv_tree_select.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P]
+    lib.tv_tree_select.restype = I
     lib.tv_philox_uniforms.argtypes = [U64, P, I, P, P, P]
     lib.tv_philox_uniforms.restype = I
     _lib = lib
@@ -244,6 +250,84 @@ def spec_accept(q_logits, p_logits, draft_tokens, parent, seed: int = 0, tempera
                                      N, V, int(seed) & 0xFFFFFFFFFFFFFFFF, float(temperature), flags, _ptr(acc_len),
                                      _ptr(acc_nodes), _ptr(toks), _ptr(ws), nbytes, _stream(dev)))
     return acc_len, acc_nodes, toks
+
+
+def commit_kv(K_tree, V_tree, accept_len, accepted_nodes, cache_len, K_cache, V_cache):
+    """Append each sequence's root and accepted path (K/V_tree bf16 [B,N,Hkv,D])
+    to K/V_cache bf16 [B,Hkv,L,D] in place at its committed length
+    (cache_len int32 [B]) -> (new_cache_len int32 [B], seq_status int32 [B])."""
+    _need(K_tree, "K_tree", torch.bfloat16, 4)
+    dev = K_tree.device
+    B, N, Hkv, D = K_tree.shape
+    _need(V_tree, "V_tree", torch.bfloat16, 4, dev)
+    for name, t in (("K_cache", K_cache), ("V_cache", V_cache)):
+        _need(t, name, torch.bfloat16, 4, dev)
+    L = K_cache.shape[2]
+    if tuple(V_tree.shape) != (B, N, Hkv, D) or tuple(K_cache.shape) != (B, Hkv, L, D) or \
+            tuple(V_cache.shape) != (B, Hkv, L, D):
+        raise ValueError("K/V_tree must be [B,N,Hkv,D] and K/V_cache [B,Hkv,L,D]")
+    _need(accept_len, "accept_len", torch.int32, 1, dev)
+    _need(accepted_nodes, "accepted_nodes", torch.int32, 2, dev)
+    _need(cache_len, "cache_len", torch.int32, 1, dev)
+    if accept_len.shape[0] != B or tuple(accepted_nodes.shape) != (B, N) or cache_len.shape[0] != B:
+        raise ValueError("accept_len, cache_len must be [B] and accepted_nodes [B,N]")
+    new_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check("tv_commit_kv",
+           _load().tv_commit_kv(_ptr(K_tree), _ptr(V_tree), _ptr(accept_len), _ptr(accepted_nodes), _ptr(cache_len),
+                                _ptr(K_cache), _ptr(V_cache), _ptr(new_len), _ptr(status), B, N, Hkv, D, L,
+                                _stream(dev)))
+    return new_len, status
+
+
+def tree_pool(B: int, P: int, device):
+    """An empty node pool for dynamic tree construction: (value fp32 [B,P],
+    parent int32 [B,P], token int32 [B,P])."""
+    return (torch.full((B, P), float("-inf"), dtype=torch.float32, device=device),
+            torch.full((B, P), -1, dtype=torch.int32, device=device),
+            torch.full((B, P), -1, dtype=torch.int32, device=device))
+
+
+def tree_expand(draft_logits, frontier, pool, pool_base: int, topk: int, n_next: int, temperature: float = 1.0,
+                root_token: Optional[torch.Tensor] = None):
+    """One expansion step (frontier None: the root).  draft_logits fp32 [B,F,V];
+    pool from tree_pool(), updated in place -> next frontier int32 [B,n_next]."""
+    _need(draft_logits, "draft_logits", torch.float32, 3)
+    dev = draft_logits.device
+    B, F, V = draft_logits.shape
+    if frontier is not None:
+        _need(frontier, "frontier", torch.int32, 2, dev)
+        if tuple(frontier.shape) != (B, F):
+            raise ValueError("frontier must be [B,F]")
+    score, parent, token = pool
+    Pn = score.shape[1]
+    for name, t, dt in (("pool value", score, torch.float32), ("pool parent", parent, torch.int32),
+                        ("pool token", token, torch.int32)):
+        _need(t, name, dt, 2, dev)
+        if tuple(t.shape) != (B, Pn):
+            raise ValueError("pool arrays must be [B,P]")
+    rt = _seq_array(root_token, "root_token", B, dev)
+    nxt = torch.empty((B, n_next), dtype=torch.int32, device=dev)
+    _check("tv_tree_expand",
+           _load().tv_tree_expand(_ptr(draft_logits), _ptr(frontier), _ptr(rt), B, F, V, int(topk), float(temperature),
+                                  _ptr(score), _ptr(parent), _ptr(token), Pn, int(pool_base),
+                                  _ptr(nxt) if n_next else None, int(n_next), _stream(dev)))
+    return nxt
+
+
+def tree_select(pool, pool_count: int, M: int):
+    """The root plus the M - 1 most valuable pool nodes, renumbered ->
+    (parent int32 [B,M], tokens int32 [B,M], pool_index int32 [B,M],
+    seq_nodes int32 [B])."""
+    score, parent, token = pool
+    dev = score.device
+    B, Pn = score.shape
+    outs = [torch.empty((B, M), dtype=torch.int32, device=dev) for _ in range(3)]
+    nodes = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check("tv_tree_select",
+           _load().tv_tree_select(_ptr(score), _ptr(parent), _ptr(token), B, Pn, int(pool_count), int(M),
+                                  *(_ptr(o) for o in outs), _ptr(nodes), _stream(dev)))
+    return outs[0], outs[1], outs[2], nodes
 
 
 def philox_uniforms(seed: int, triples: torch.Tensor):

@@ -354,9 +354,14 @@ __device__ void merge_partials(const AttnArgs& a, char* lds, int grp, int row0, 
 template <int NT, int ROWS>
 __device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp, int row0, int nrows, int b,
                              int g) {
-    // every wave releases its partial stores at agent scope, the barrier orders
-    // them before the arrival; the last workgroup acquires before it reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // Every wave waits until its partial stores have completed, the barrier
+    // orders them before thread 0's arrival, and that arrival is a release at
+    // agent scope (it writes back what this XCD's L2 holds for other XCDs); the
+    // last workgroup's arrival is also an acquire, and its barrier orders every
+    // wave's loads after it (the loads are device-coherent besides).  One fence
+    // per workgroup: a release fence in every wave cost 2-3 us per call on the
+    // single-sequence workloads.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev =
@@ -365,7 +370,6 @@ __device__ void merge_splits(const AttnArgs& a, char* lds, int* s_flag, int grp,
     }
     __syncthreads();
     if (!*s_flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (nrows <= 0) {  // a row tile of padding nodes only (ragged batch): nothing to merge
         if (threadIdx.x == 0) __hip_atomic_store(&a.counter[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
