@@ -261,13 +261,16 @@ def counted_traffic(workload, kernel_key, files):
     return None if rec is None else int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
 
-def counted_mfma(workload, files):
-    """MFMA counters of the attention kernel on ``workload`` from the committed
-    summary: busy fraction of the matrix pipes and the MFMA FLOPs issued."""
+def counted_mfma(workload, files, avg_us):
+    """MFMA FLOPs the attention kernel issues per launch on ``workload``, from
+    the committed counter summary (calibrated against the probe's MFMA loop),
+    and their rate over the live duration as a fraction of the bf16 peak."""
     rec = _profile_record(f"mfma_{workload}.md", "tree_attention_kernel", files)
     if rec is None:
         return None
-    return {k: rec[k] for k in ("mfma_busy_frac", "mfma_flops_issued", "mfma_flops_per_alg_flop") if k in rec}
+    issued = float(rec["mfma_flops_issued"])
+    return {"flops_issued": issued, "per_alg_flop": rec["mfma_flops_per_alg_flop"],
+            "util": round(issued / (avg_us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4)}
 
 
 def cpu_baseline(w, inputs, temperature, seconds):
@@ -398,7 +401,7 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
         roof["algorithmic_flops"] = a_flops
         roof["avg_us"] = round(per["attention"] * 1e3, 3)
         roof["traffic"] = counted_traffic(w.name, "tree_attention_kernel", ATTN_SOURCES)
-        mf = counted_mfma(w.name, ATTN_SOURCES)
+        mf = counted_mfma(w.name, ATTN_SOURCES, per["attention"] * 1e3)
         if mf is not None:
             roof["mfma_counters"] = mf
     else:
