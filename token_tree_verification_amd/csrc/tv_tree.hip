@@ -31,47 +31,6 @@ constexpr int kMaxPool = 4096;
 // Larger value wins; equal values go to the smaller index.
 __device__ __forceinline__ bool better(float v, int i, float v2, int i2) { return v > v2 || (v == v2 && i < i2); }
 
-// A thread's top K of the elements it saw, sorted best first (registers; the
-// insertion is unrolled so no array is indexed dynamically).
-template <int K>
-struct TopK {
-    float v[K];
-    int i[K];
-    __device__ __forceinline__ void init() {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            v[k] = -INFINITY;
-            i[k] = 0x7fffffff;
-        }
-    }
-    __device__ __forceinline__ void offer(float x, int idx) {
-        if (!better(x, idx, v[K - 1], i[K - 1])) return;
-        // from the end: shift worse entries down one place, drop x in the gap
-        bool placed = false;
-#pragma unroll
-        for (int k = K - 1; k >= 0; --k) {
-            if (placed) continue;
-            if (k > 0 && better(x, idx, v[k - 1], i[k - 1])) {
-                v[k] = v[k - 1];
-                i[k] = i[k - 1];
-            } else {
-                v[k] = x;
-                i[k] = idx;
-                placed = true;
-            }
-        }
-    }
-    __device__ __forceinline__ void pop() {
-#pragma unroll
-        for (int k = 0; k < K - 1; ++k) {
-            v[k] = v[k + 1];
-            i[k] = i[k + 1];
-        }
-        v[K - 1] = -INFINITY;
-        i[K - 1] = 0x7fffffff;
-    }
-};
-
 struct ExpandArgs {
     const float* logits;      // [B][F][V]
     const int32_t* frontier;  // [B][F] pool slots, or null: the root
@@ -83,13 +42,67 @@ struct ExpandArgs {
     double inv_t;             // 1 / T
 };
 
-// One workgroup per (sequence, frontier row): a streamed pass (16-byte loads,
-// the next chunk in flight while one is processed) keeps each thread's
-// running maximum, its fp64 sum of exp((x - max) / T) (rescaled when the
-// maximum rises; the exponentials in fp64, four independent ones per chunk)
-// and its top K logits; the block then merges the threads' lists in topk
-// rounds and writes the candidates.
-template <int K, bool VEC4>
+// Wave-level top-k: each wave keeps, in LDS, its best k elements so far
+// (sorted best first) followed by the new elements that beat the k-th of them;
+// a ballot compacts those into the buffer, and when the buffer could overflow
+// the wave re-selects its best k from it (k rounds of a wave argmax).  After
+// the first few batches almost nothing beats the k-th best, so an element
+// costs one comparison.  (A per-thread sorted list instead made nearly every
+// element run the insertion in some lane of the wave.)
+constexpr int kCandCap = 4 * kWave * 2 + kMaxTopK;  // two batches of candidates plus the kept k
+
+struct WaveTop {
+    float* v;  // [kCandCap] this wave's buffer in LDS
+    int* i;
+};
+
+// Re-select the best k of the first n buffer entries into entries 0..k-1
+// (sorted best first); returns the new count (min(n, k)).  Wave-uniform.
+__device__ int wave_select(WaveTop t, int n, int k) {
+    const int lane = threadIdx.x & 63;
+    // the selected entries go to a scratch tail and are copied back at the end
+    float* ov = t.v + kCandCap - kMaxTopK;
+    int* oi = t.i + kCandCap - kMaxTopK;
+    const int m = min(n, k);
+    for (int j = 0; j < m; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff, bp = -1;
+        for (int p = lane; p < n; p += kWave) {
+            const float v = t.v[p];
+            const int i = t.i[p];
+            if (bp < 0 || better(v, i, bv, bi)) {
+                bv = v;
+                bi = i;
+                bp = p;
+            }
+        }
+        int key = bi;
+        float kv = bv;
+        group_argmax_dpp(kv, key, kWave);  // ties to the smaller index
+        // the lane holding the winner removes it
+        if (bp >= 0 && bi == key && bv == kv) t.i[bp] = 0x7fffffff, t.v[bp] = -INFINITY;
+        if (lane == 0) {
+            ov[j] = kv;
+            oi[j] = key;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    for (int j = lane; j < m; j += kWave) {
+        t.v[j] = ov[j];
+        t.i[j] = oi[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    return m;
+}
+
+// One workgroup per (sequence, frontier row).  Wave w streams batches of 256
+// logits w, w + 8, ... (16-byte loads, the next batch in flight); each lane
+// keeps its running maximum and an fp64 sum of exp((x - max) / T) (our fp64
+// exponential, four independent ones per batch, rescaled when the maximum
+// rises); the wave keeps its top k as above.  The block then combines the
+// waves' maxima and sums (waves in order) and wave 0 selects the row's top k
+// from the eight wave lists.
+template <bool VEC4>
 __global__ __launch_bounds__(kExpandThreads) void expand_rows_kernel(const ExpandArgs a) {
     const int b = blockIdx.y, f = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -109,62 +122,84 @@ __global__ __launch_bounds__(kExpandThreads) void expand_rows_kernel(const Expan
         return;
     }
     __shared__ double s_tab[32];
-    __shared__ float s_wv[kExpandWaves];
-    __shared__ int s_wi[kExpandWaves];
+    __shared__ float s_cv[kExpandWaves][kCandCap];
+    __shared__ int s_ci[kExpandWaves][kCandCap];
     __shared__ double s_ws[kExpandWaves];
     __shared__ float s_wm[kExpandWaves];
-    __shared__ int s_pick;
+    __shared__ int s_wn[kExpandWaves];
     if (tid < 32) exp2_table(s_tab, tid);
     __syncthreads();
 
     const float* row = a.logits + ((size_t)b * a.F + f) * a.V;
     const double inv_t = a.inv_t;
-    const int V = a.V;
-    TopK<K> top;
-    top.init();
+    const int V = a.V, k = a.topk;
+    WaveTop top{s_cv[wave], s_ci[wave]};
+    int n = 0;                       // buffer entries (wave-uniform)
+    float tv = -INFINITY;            // the k-th best so far (wave-uniform), or none yet
+    int ti = 0x7fffffff;
+    bool full = false;
     float m = -INFINITY;
     double s = 0.0;
-    // chunk c covers elements 4c .. 4c+3; thread tid takes chunks tid, tid + T, ...
-    const int nchunk = (V + 3) / 4;
-    auto load = [&](int ch) {
+    const int nbatch = (V + 4 * kWave - 1) / (4 * kWave);
+    auto load = [&](int bt) {
         f32x4 x;
-        const int e = 4 * min(ch, nchunk - 1);
+        const int e = 4 * (min(bt, nbatch - 1) * kWave + lane);
         if constexpr (VEC4) {
-            x = *reinterpret_cast<const f32x4*>(row + e);
+            x = *reinterpret_cast<const f32x4*>(row + min(e, V - 4));
         } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) x[k] = row[min(e + k, V - 1)];
+            for (int q = 0; q < 4; ++q) x[q] = row[min(e + q, V - 1)];
         }
         return x;
     };
-    auto process = [&](const f32x4& x, int ch) {
-        const int e = 4 * ch;
-        f32x4 y = x;
+    int bt = wave;
+    f32x4 cur = load(bt);
+    while (bt < nbatch) {
+        const int nx = bt + kExpandWaves;
+        const f32x4 nxt = load(nx);
+        const int e = 4 * (bt * kWave + lane);
+        f32x4 y = cur;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (e + k >= V) y[k] = -INFINITY;
+        for (int q = 0; q < 4; ++q)
+            if (e + q >= V) y[q] = -INFINITY;
+        // softmax statistics
         const float m4 = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
         if (m4 > m) {
             if (m != -INFINITY) s *= exp_nonpos(((double)m - (double)m4) * inv_t, s_tab);
             m = m4;
         }
-        double e01 = exp_nonpos(((double)y[0] - (double)m) * inv_t, s_tab) +
-                     exp_nonpos(((double)y[1] - (double)m) * inv_t, s_tab);
-        double e23 = exp_nonpos(((double)y[2] - (double)m) * inv_t, s_tab) +
-                     exp_nonpos(((double)y[3] - (double)m) * inv_t, s_tab);
-        s += e01 + e23;
+        if (m != -INFINITY) {
+            const double e01 = exp_nonpos(((double)y[0] - (double)m) * inv_t, s_tab) +
+                               exp_nonpos(((double)y[1] - (double)m) * inv_t, s_tab);
+            const double e23 = exp_nonpos(((double)y[2] - (double)m) * inv_t, s_tab) +
+                               exp_nonpos(((double)y[3] - (double)m) * inv_t, s_tab);
+            s += e01 + e23;
+        }
+        // candidates: valid elements that beat the k-th best so far
 #pragma unroll
-        for (int k = 0; k < 4; ++k) top.offer(y[k], e + k);
-    };
-    int ch = tid;
-    f32x4 cur = load(ch);
-    while (ch < nchunk) {
-        const int nx = ch + kExpandThreads;
-        const f32x4 nxt = load(nx);
-        process(cur, ch);
+        for (int q = 0; q < 4; ++q) {
+            const bool pass = e + q < V && (!full || better(y[q], e + q, tv, ti));
+            const uint64_t bal = __ballot(pass);
+            if (pass) {
+                const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
+                top.v[pos] = y[q];
+                top.i[pos] = e + q;
+            }
+            n += __popcll(bal);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (n > kCandCap - kMaxTopK - 4 * kWave) {  // the next batch could overflow: re-select
+            n = wave_select(top, n, k);
+            full = n >= k;
+            if (full) {
+                tv = top.v[k - 1];
+                ti = top.i[k - 1];
+            }
+        }
         cur = nxt;
-        ch = nx;
+        bt = nx;
     }
+    n = wave_select(top, n, k);
     // row maximum and sum over the block (fixed association: waves in order)
     const float wm = group_max_dpp(m, kWave);
     const double ws = group_sum_dpp(m == -INFINITY ? 0.0 : s * exp_nonpos(((double)m - (double)wm) * inv_t, s_tab),
@@ -172,64 +207,65 @@ __global__ __launch_bounds__(kExpandThreads) void expand_rows_kernel(const Expan
     if (lane == 0) {
         s_wm[wave] = wm;
         s_ws[wave] = ws;
+        s_wn[wave] = n;
     }
     __syncthreads();
+    if (wave != 0) return;
     float M = s_wm[0];
-    for (int k = 1; k < kExpandWaves; ++k) M = fmaxf(M, s_wm[k]);
+    for (int q = 1; q < kExpandWaves; ++q) M = fmaxf(M, s_wm[q]);
     double S = 0.0;
-    for (int k = 0; k < kExpandWaves; ++k)
-        if (s_wm[k] != -INFINITY) S += s_ws[k] * exp_nonpos(((double)s_wm[k] - (double)M) * inv_t, s_tab);
+    for (int q = 0; q < kExpandWaves; ++q)
+        if (s_wm[q] != -INFINITY) S += s_ws[q] * exp_nonpos(((double)s_wm[q] - (double)M) * inv_t, s_tab);
     const double lse = log(S);
     const float parent_score = a.frontier ? a.score[(size_t)b * a.P + slot] : 0.f;
-
-    // topk rounds: the block's best head wins and its thread pops it
-    for (int j = 0; j < a.topk; ++j) {
-        float bv = top.v[0];
-        int bi = top.i[0];
-        group_argmax_dpp(bv, bi, kWave);
-        if (lane == 0) {
-            s_wv[wave] = bv;
-            s_wi[wave] = bi;
+    // gather the waves' lists into wave 0's buffer (after its own k entries)
+    int cnt = s_wn[0];
+    for (int w = 1; w < kExpandWaves; ++w) {
+        const int nw = s_wn[w];
+        for (int j = lane; j < nw; j += kWave) {
+            top.v[cnt + j] = s_cv[w][j];
+            top.i[cnt + j] = s_ci[w][j];
         }
-        __syncthreads();
-        if (tid == 0) {
-            float v0 = s_wv[0];
-            int i0 = s_wi[0];
-            for (int k = 1; k < kExpandWaves; ++k)
-                if (better(s_wv[k], s_wi[k], v0, i0)) {
-                    v0 = s_wv[k];
-                    i0 = s_wi[k];
-                }
-            s_pick = i0;
-            const bool valid = i0 < V;  // fewer tokens than topk: the rest stay empty
-            const double lp = ((double)v0 - (double)M) * inv_t - lse;
-            a.score[out0 + j] = valid ? (float)((double)parent_score + lp) : -INFINITY;
-            a.parent[out0 + j] = valid ? slot : -1;
-            a.token[out0 + j] = valid ? i0 : -1;
-        }
-        __syncthreads();
-        if (top.i[0] == s_pick) top.pop();
-        __syncthreads();
+        cnt += nw;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int got = wave_select(top, cnt, k);
+    for (int j = lane; j < k; j += kWave) {
+        const bool valid = j < got && top.i[j] < V;  // fewer tokens than topk: the rest stay empty
+        const double lp = ((double)top.v[j] - (double)M) * inv_t - lse;
+        a.score[out0 + j] = valid ? (float)((double)parent_score + lp) : -INFINITY;
+        a.parent[out0 + j] = valid ? slot : -1;
+        a.token[out0 + j] = valid ? top.i[j] : -1;
     }
 }
 
 // Next frontier: the Fn best of this step's candidates (slots base ..
-// base + C - 1) by (value, slot); empty candidates never qualify.
+// base + C - 1) by (value, slot); empty candidates never qualify.  One thread
+// per candidate counts the candidates that beat it (staged in LDS when they
+// fit).
 __global__ __launch_bounds__(kSelectThreads) void pick_frontier_kernel(const float* __restrict__ score,
                                                                        const int32_t* __restrict__ parent, int P,
                                                                        int base, int C, int32_t* __restrict__ next,
                                                                        int Fn) {
     const int b = blockIdx.x;
+    __shared__ float s_sc[kMaxPool];
     for (int k = threadIdx.x; k < Fn; k += kSelectThreads) next[(size_t)b * Fn + k] = -1;
-    __syncthreads();
     const float* sc = score + (size_t)b * P + base;
     const int32_t* pa = parent + (size_t)b * P + base;
+    const bool staged = C <= kMaxPool;
+    if (staged)  // empty candidates enter as NaN, which never beats or ties anything
+        for (int i = threadIdx.x; i < C; i += kSelectThreads) s_sc[i] = pa[i] >= 0 ? sc[i] : __builtin_nanf("");
+    __syncthreads();
     for (int i = threadIdx.x; i < C; i += kSelectThreads) {
         if (pa[i] < 0) continue;
         const float si = sc[i];
         int rank = 0;
-        for (int j = 0; j < C; ++j)
-            if (pa[j] >= 0 && better(sc[j], j, si, i)) ++rank;
+        if (staged) {
+            for (int j = 0; j < C; ++j) rank += better(s_sc[j], j, si, i);
+        } else {
+            for (int j = 0; j < C; ++j)
+                if (pa[j] >= 0 && better(sc[j], j, si, i)) ++rank;
+        }
         if (rank < Fn) next[(size_t)b * Fn + rank] = base + i;
     }
 }
@@ -305,12 +341,11 @@ __global__ __launch_bounds__(kSelectThreads) void select_tree_kernel(const float
     if (threadIdx.x == 0) out_nodes[b] = n;
 }
 
-template <int K>
 int launch_expand(const ExpandArgs& a, int B, int Frows, bool vec4, hipStream_t st) {
     if (vec4)
-        hipLaunchKernelGGL((expand_rows_kernel<K, true>), dim3(Frows, B), dim3(kExpandThreads), 0, st, a);
+        hipLaunchKernelGGL((expand_rows_kernel<true>), dim3(Frows, B), dim3(kExpandThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((expand_rows_kernel<K, false>), dim3(Frows, B), dim3(kExpandThreads), 0, st, a);
+        hipLaunchKernelGGL((expand_rows_kernel<false>), dim3(Frows, B), dim3(kExpandThreads), 0, st, a);
     return launch_status();
 }
 
@@ -346,17 +381,7 @@ extern "C" int tv_tree_expand(const float* draft_logits, const int32_t* frontier
     a.inv_t = 1.0 / (double)temperature;
     hipStream_t st = (hipStream_t)stream;
     const bool vec4 = V % 4 == 0 && aligned(draft_logits, 16);
-    int rc;
-    if (topk <= 1)
-        rc = launch_expand<1>(a, B, F, vec4, st);
-    else if (topk <= 2)
-        rc = launch_expand<2>(a, B, F, vec4, st);
-    else if (topk <= 4)
-        rc = launch_expand<4>(a, B, F, vec4, st);
-    else if (topk <= 8)
-        rc = launch_expand<8>(a, B, F, vec4, st);
-    else
-        rc = launch_expand<16>(a, B, F, vec4, st);
+    const int rc = launch_expand(a, B, F, vec4, st);
     if (rc != TV_OK || Fn == 0) return rc;
     hipLaunchKernelGGL(pick_frontier_kernel, dim3(B), dim3(kSelectThreads), 0, st, pool_score, pool_parent, P,
                        pool_base, F * topk, next_frontier, Fn);
