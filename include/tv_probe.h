@@ -23,10 +23,13 @@ extern "C" {
 int tv_probe_stream_read(const void* src, size_t bytes, float* out, int nblocks, void* stream);
 
 /* `nblocks` workgroups of four waves; each wave issues `iters` rounds of four
- * independent v_mfma_f32_32x32x16_bf16 on register operands.  Writes one float
- * per thread to out[nblocks * 256].  FLOPs per launch:
- * tv_probe_mfma_loop_flops(nblocks, iters). */
-int tv_probe_mfma_loop(int nblocks, int iters, float* out, void* stream);
+ * independent v_mfma_f32_32x32x16_bf16 on register operands: constant ones
+ * (random_operands == 0: few bits toggle, the clock stays near its maximum)
+ * or random ones, a different pair per chain (the power drawn by real data,
+ * at the lower clock the chip then holds).  Writes one float per thread to
+ * out[nblocks * 256].  FLOPs per launch: tv_probe_mfma_loop_flops(nblocks,
+ * iters). */
+int tv_probe_mfma_loop(int nblocks, int iters, int random_operands, float* out, void* stream);
 
 /* 2 * 32 * 32 * 16 * 4 * iters * 4 * nblocks. */
 double tv_probe_mfma_loop_flops(int nblocks, int iters);

@@ -903,14 +903,21 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         dk[i] = (uint32_t)(key * kRowBytes + ((pc ^ (key & 15)) << 4));
         dv[i] = (uint32_t)(key * kRowBytes + ((pc ^ (4 * (key & 3))) << 4));
     }
+    // The four base pointers stay in SGPRs across the loop (selected from the
+    // argument block, they would be reloaded, with a wait, every tile).
+    const uint16_t* kc_p = a.Kc;
+    const uint16_t* kt_p = a.Kt;
+    const uint16_t* vc_p = a.Vc;
+    const uint16_t* vt_p = a.Vt;
+    asm volatile("" : "+s"(kc_p), "+s"(kt_p), "+s"(vc_p), "+s"(vt_p));
     auto issue_dma = [&](int u) {
         // (uniform selects rather than branches for the source)
         const int tt = min(u, nt - 1);
         const bool tree = tt >= n_cache;
         const int key0 = tree ? (tt - n_cache) * KT : (t_begin + tt) * KT;
         const size_t base = tree ? ((size_t)(b * a.N + key0) * a.Hkv + g) * HD : ((size_t)bg * a.L + key0) * HD;
-        const char* ks = reinterpret_cast<const char*>((tree ? a.Kt : a.Kc) + base);
-        const char* vs = reinterpret_cast<const char*>((tree ? a.Vt : a.Vc) + base);
+        const char* ks = reinterpret_cast<const char*>((tree ? kt_p : kc_p) + base);
+        const char* vs = reinterpret_cast<const char*>((tree ? vt_p : vc_p) + base);
         const uint32_t stride = tree ? (uint32_t)a.Hkv * kRowBytes : (uint32_t)kRowBytes;
         const int nk = min(KT, (tree ? a.N : lb) - key0);
         const uint32_t dst = stage(u) + r0 * kRowBytes;

@@ -7,7 +7,11 @@
 //  * mfma_loop: every wave runs four independent chains of
 //    v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 multiply-adds each) on register
 //    operands; nothing else in the loop.  Its FLOP/s is the dense bf16 MFMA
-//    rate the chip sustains at the clock it holds under that load.
+//    rate the chip sustains at the clock it holds under that load.  With
+//    constant operands few bits toggle and the clock stays near its maximum;
+//    with random operands (a different pair for each chain, drawn from a
+//    hash of the thread and workgroup) the power drawn is that of real data
+//    and the clock the chip holds is lower.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,14 +47,34 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const f32x4*
     out[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
 }
 
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    // an integer hash (xor-shift-multiply rounds) for operand values
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+template <bool RANDOM>
 __global__ __launch_bounds__(kProbeThreads) void mfma_loop_kernel(int iters, float* __restrict__ out) {
     const int t = threadIdx.x;
-    bf16x8 a, b;
+    bf16x8 a[kChains], b[kChains];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        a[k] = (__bf16)(0.001f * (float)((t + k) & 15));
-        b[k] = (__bf16)(0.002f * (float)((t * 3 + k) & 15));
-    }
+    for (int c = 0; c < kChains; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (RANDOM) {
+                // values in [-2, 2): every mantissa bit of the bf16 varies
+                const uint32_t h = mix32((uint32_t)(t * 131 + blockIdx.x * 7919 + c * 17 + k));
+                a[c][k] = (__bf16)((float)((int)(h & 0xffff) - 32768) * (1.f / 16384.f));
+                b[c][k] = (__bf16)((float)((int)(h >> 16) - 32768) * (1.f / 16384.f));
+            } else {
+                a[c][k] = (__bf16)(0.001f * (float)((t + k) & 15));
+                b[c][k] = (__bf16)(0.002f * (float)((t * 3 + k) & 15));
+            }
+        }
     f32x16 acc[kChains];
 #pragma unroll
     for (int c = 0; c < kChains; ++c)
@@ -58,7 +82,8 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_loop_kernel(int iters, flo
         for (int k = 0; k < 16; ++k) acc[c][k] = 0.f;
     for (int i = 0; i < iters; ++i) {
 #pragma unroll
-        for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+        for (int c = 0; c < kChains; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[(c + 1) % kChains], acc[c], 0, 0, 0);
     }
     float s = 0.f;
 #pragma unroll
@@ -77,9 +102,14 @@ extern "C" int tv_probe_stream_read(const void* src, size_t bytes, float* out, i
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-extern "C" int tv_probe_mfma_loop(int nblocks, int iters, float* out, void* stream) {
+extern "C" int tv_probe_mfma_loop(int nblocks, int iters, int random_operands, float* out, void* stream) {
     if (!out || nblocks < 1 || iters < 1) return -1;
-    hipLaunchKernelGGL(mfma_loop_kernel, dim3(nblocks), dim3(kProbeThreads), 0, (hipStream_t)stream, iters, out);
+    if (random_operands)
+        hipLaunchKernelGGL(mfma_loop_kernel<true>, dim3(nblocks), dim3(kProbeThreads), 0, (hipStream_t)stream, iters,
+                           out);
+    else
+        hipLaunchKernelGGL(mfma_loop_kernel<false>, dim3(nblocks), dim3(kProbeThreads), 0, (hipStream_t)stream, iters,
+                           out);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
