@@ -814,18 +814,21 @@ __device__ __forceinline__ uint32_t pack_f16(float x, float y) {
 //                                register refilled with V(j)^T after its MFMA
 //   S(j+1) = K(j+1) Q^T          8 bf16 MFMAs, each K fragment register
 //                                refilled with K(j+2)
-// so that a wave's exponentials run under its own matrix products (vector
-// work of the other wave on the SIMD fills MFMA gaps poorly on this chip).
-// The running max is decided before the stream; a raise rescales O after it,
-// once P(j-1) V(j-1) is in.
+// so that a wave's exponentials run under its own matrix products.  The
+// running max is tested before the stream (one compare and a uniform branch;
+// a rise is rare after the first block); a raise rescales O after it, once
+// P(j-1) V(j-1) is in.
 //
-// Ring.  Tiles go from HBM to LDS by direct DMA, three tiles ahead.  Wave w
-// copies the 8 keys that form one MFMA k-group of V: 16-key step w/2, key
-// half w%2, i.e. keys 16 (w/2) + 4 (w%2) + {0..3} and the same + 8.  After
-// its own copies land it converts them alone: transposing reads of its 8 bf16
-// rows give each lane the 8 keys at one head dim, rounded to fp16 and written
-// back over the same 2 KB (dims 0-63 over the first four rows, 64-127 over
-// the second), so a V^T fragment is one 16-byte read.  K stays as copied
+// Ring.  Tiles go from HBM to LDS by direct DMA, three tiles ahead, in eight
+// key groups: group k holds the 8 keys that form one MFMA k-group of V,
+// 16-key step k/2, key half k%2, i.e. keys 16 (k/2) + 4 (k%2) + {0..3} and
+// the same + 8.  Waves 0-3 copy groups w and w+4 (32 keys further on); waves
+// 4-7 copy nothing.  The older wave of each SIMD is favoured by the issue
+// arbiter and would otherwise wait at the tile's barrier for the younger one.
+// After a wave's own copies land it converts them alone: transposing reads of
+// a group's 8 bf16 rows give each lane the 8 keys at one head dim, rounded to
+// fp16 and written back over the same 2 KB (dims 0-63 over the first four
+// rows, 64-127 over the second), so a V^T fragment is one 16-byte read.  K stays as copied
 // (16-byte chunks of key k at chunk ^ (k & 15)); V rows are copied with chunk
 // ^ 4 (k & 3) so that the transposing reads are conflict-free.  One workgroup
 // barrier per tile: tile t starts by issuing the DMA of tile t+3 (into the
@@ -889,10 +892,11 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     const uint32_t ring_addr = (uint32_t)(uintptr_t)(lds_void*)lds;
     auto stage = [&](int t) { return ring_addr + (uint32_t)(t % S) * STAGE; };
 
-    // ---- this wave's 8 keys of every tile: rows r0 .. r0+3 and r0+8 .. r0+11 ----
+    // ---- key group of this wave (waves 0-3 also copy group wave+4, rows
+    // +32): rows r0 .. r0+3 and r0+8 .. r0+11 ----
     const int r0 = 16 * (wave >> 1) + 4 * (wave & 1);
-    // DMA of this wave's rows of tile u into stage u % S (1 KB = four rows per
-    // copy).  Past the last tile the last tile is loaded again into the
+    // DMA of a key group (rows r0 + roff ..) of tile u into stage u % S (1 KB
+    // = four rows per copy).  Past the last tile the last tile is loaded again into the
     // (free) stage, so that every tile issues the same copies and the wait
     // counts stay static.  Per-lane byte offsets of a full cache tile's
     // copies are kept; other tiles recompute them.
@@ -910,7 +914,7 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     const uint16_t* vc_p = a.Vc;
     const uint16_t* vt_p = a.Vt;
     asm volatile("" : "+s"(kc_p), "+s"(kt_p), "+s"(vc_p), "+s"(vt_p));
-    auto issue_dma = [&](int u) {
+    auto issue_dma = [&](int u, int roff) {
         // (uniform selects rather than branches for the source)
         const int tt = min(u, nt - 1);
         const bool tree = tt >= n_cache;
@@ -920,12 +924,12 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         const char* vs = reinterpret_cast<const char*>((tree ? vt_p : vc_p) + base);
         const uint32_t stride = tree ? (uint32_t)a.Hkv * kRowBytes : (uint32_t)kRowBytes;
         const int nk = min(KT, (tree ? a.N : lb) - key0);
-        const uint32_t dst = stage(u) + r0 * kRowBytes;
+        const uint32_t dst = stage(u) + (r0 + roff) * kRowBytes;
         if (!tree && nk == KT) {  // uniform: a full cache tile
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                dma16s(ks, dk[i], dst + 8 * i * kRowBytes);
-                dma16s(vs, dv[i], dst + TILE + 8 * i * kRowBytes);
+                dma16s(ks + roff * kRowBytes, dk[i], dst + 8 * i * kRowBytes);
+                dma16s(vs + roff * kRowBytes, dv[i], dst + TILE + 8 * i * kRowBytes);
             }
             return;
         }
@@ -933,13 +937,14 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         asm volatile("" : "+v"(l));  // recomputed per call rather than held in registers
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int key = r0 + 8 * i + (l >> 4), pc = l & 15;
+            const int key = r0 + roff + 8 * i + (l >> 4), pc = l & 15;
             const uint32_t off = (uint32_t)min(key, nk - 1) * stride;  // ragged keys repeat a valid row
             dma16s(ks, off + ((pc ^ (key & 15)) << 4), dst + 8 * i * kRowBytes);
             dma16s(vs, off + ((pc ^ (4 * (key & 3))) << 4), dst + TILE + 8 * i * kRowBytes);
         }
     };
-    // In-place conversion of this wave's V rows of tile u.  Transposing read
+    // In-place conversion of a key group's V rows of tile u (rows r0 + roff
+    // ..; roff = 32 keeps every bank pattern below).  Transposing read
     // (dims half hh, rows part p): in each 16-lane group, source lane j reads
     // row r0 + 8p + j/4 at head dims 64 hh + 16 (lane/16) + 4 (j%4) + {0..3},
     // so result lane i of the group holds rows r0 + 8p + {0..3} at dim
@@ -949,8 +954,8 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     const uint32_t conv_src = (uint32_t)(TILE + (r0 + ((lane & 15) >> 2)) * kRowBytes +
                                          (((2 * (lane >> 4) + ((lane & 3) >> 1)) ^ (4 * ((lane & 15) >> 2))) << 4) +
                                          8 * (lane & 1));
-    auto convert = [&](int u) {
-        uint32_t sb = stage(u);
+    auto convert = [&](int u, int roff) {
+        uint32_t sb = stage(u) + roff * kRowBytes;
         asm volatile("" : "+v"(sb));
         u32x2 part[2][2];  // [dims half][rows part]
 #pragma unroll
@@ -995,6 +1000,11 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     u32x4 pf[2];     // P(j-1)
     float m_used = -INFINITY;  // raw score units
     float l_run = 0.f;
+    // derived from m_used, updated only when it rises: the raise threshold,
+    // -m_used * c (0 while m_used is -inf) and the lanes whose m_used is -inf
+    float m_thr = -INFINITY;
+    float neg_mc = 0.f;
+    uint64_t m_ninf = ~0ull;
 
     // block j = 2t + kb of tile t.  V(j)^T is block kb of tile t; K(j+2) is
     // block kb of tile t+1.
@@ -1033,20 +1043,25 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
                 if (!((vis >> (8 * (e >> 2) + (e & 3))) & 1u)) s_cur[e] = -INFINITY;
         }
         // lazy running max: raised only when a score exceeds it by 2^kLazyThresh
+        // (one v_max3 per pair of scores)
         float tmax = fmaxf(s_cur[0], s_cur[1]);
 #pragma unroll
-        for (int e = 2; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s_cur[e], s_cur[e + 1]));
+        for (int e = 2; e < 16; e += 2) tmax = fmaxf(fmaxf(tmax, s_cur[e]), s_cur[e + 1]);
         tmax = halves_max(tmax);
-        const bool raise = tmax > m_used + kLazyThresh / c || m_used == -INFINITY;
-        const bool any_raise = __ballot(raise) != 0;
+        const uint64_t rmask = __ballot(tmax > m_thr) | m_ninf;
+        const bool any_raise = rmask != 0;
         float alpha = 1.f;
-        if (raise) {
-            const float m_new = fmaxf(m_used, tmax);
-            alpha = (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * c);
-            m_used = m_new;
-            l_run *= alpha;
+        if (any_raise) {  // uniform, rare after the first block
+            if ((rmask >> lane) & 1ull) {
+                const float m_new = fmaxf(m_used, tmax);
+                alpha = (m_used == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * c);
+                m_used = m_new;
+                l_run *= alpha;
+            }
+            m_thr = m_used + kLazyThresh / c;
+            neg_mc = (m_used == -INFINITY) ? 0.f : -(m_used * c);
+            m_ninf = __ballot(m_used == -INFINITY);
         }
-        const float mc = (m_used == -INFINITY) ? 0.f : m_used * c;
 
         // P(j), software-pipelined over score pairs (pair k = elements
         // 8 (k/4) + 2 (k%4) + {0, 1}): step k issues P.V MFMA k+2, the
@@ -1055,7 +1070,7 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         // MFMAs reading that half of P(j-1) are issued by then.  The sum uses
         // the fp16 values handed to the MFMA.
         const f16x2 ones = f16x2{(_Float16)1.f, (_Float16)1.f};
-        float x0 = fmaf(s_cur[0], c, -mc), x1 = fmaf(s_cur[1], c, -mc);
+        float x0 = fmaf(s_cur[0], c, neg_mc), x1 = fmaf(s_cur[1], c, neg_mc);
         float e0 = 0.f, e1 = 0.f;
 #pragma unroll
         for (int k = 0; k <= 8; ++k) {
@@ -1067,8 +1082,8 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
             }
             if (k + 1 < 8) {
                 const int e = 8 * ((k + 1) >> 2) + 2 * ((k + 1) & 3);
-                x0 = fmaf(s_cur[e], c, -mc);
-                x1 = fmaf(s_cur[e + 1], c, -mc);
+                x0 = fmaf(s_cur[e], c, neg_mc);
+                x1 = fmaf(s_cur[e + 1], c, neg_mc);
             }
             if (k >= 1) {
                 uint32_t w = pack_f16(e0, e1);
@@ -1100,11 +1115,19 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     if (nt > 0) {
         // ---- prologue: DMA of tiles 0-2; tiles 0 and 1 converted; S(0); K(1)
         // in registers; P(-1) = 0 with finite V(-1) ----
+        if (wave < 4)
 #pragma unroll
-        for (int u = 0; u < 3; ++u) issue_dma(u);
-        wait_vmcnt<4>();  // tiles 0 and 1 have landed
-        convert(0);
-        convert(1);
+            for (int u = 0; u < 3; ++u) {
+                issue_dma(u, 0);
+                issue_dma(u, 32);
+            }
+        wait_vmcnt<8>();  // tiles 0 and 1 have landed
+        if (wave < 4) {
+            convert(0, 0);
+            convert(0, 32);
+            convert(1, 0);
+            convert(1, 32);
+        }
         __syncthreads();  // tiles 0 and 1 are visible
         read_k(ring_addr, 0);
         {
@@ -1123,11 +1146,17 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
         const int n_full = (t_begin + n_cache) * KT <= lb ? n_cache : n_cache - 1;
         for (int t = 0; t < nt; ++t) {
             const bool masked = t >= n_full;  // tree tiles and a ragged last cache tile
-            issue_dma(t + 3);
+            if (wave < 4) {
+                issue_dma(t + 3, 0);
+                issue_dma(t + 3, 32);
+            }
             block(masked, t, 0);
             block(masked, t, 1);
-            wait_vmcnt<4>();  // tile t+2 has landed (tile t+3 still in flight)
-            convert(t + 2);
+            wait_vmcnt<8>();  // tile t+2 has landed (tile t+3 still in flight)
+            if (wave < 4) {
+                convert(t + 2, 0);
+                convert(t + 2, 32);
+            }
             __syncthreads();  // tile t+2 is visible; tile t-1's last reads are consumed
         }
         // the last block's P.V
