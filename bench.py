@@ -179,7 +179,7 @@ def copy_calibration(torch, dev, nbytes=COPY_CAL_BYTES):
 def achievable_peaks(torch, dev, stream):
     """The device's reachable rates in this run, beside the spec peaks: the
     probe library's streaming read (2 GiB of 16-byte loads, a contiguous range
-    per workgroup) and pure MFMA loop
+    per workgroup; ordinary and non-temporal loads) and pure MFMA loop
     (four independent v_mfma_f32_32x32x16_bf16 chains per wave, four waves per
     SIMD) on constant operands and on random ones (real data draws more power,
     so the chip holds a lower clock), a plain copy (512 MiB read plus 512 MiB written) and a library bf16
@@ -196,8 +196,8 @@ def achievable_peaks(torch, dev, stream):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps / 1e3  # seconds per call
     probe = ctypes.CDLL(PROBE_LIB)
-    probe.tv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                           ctypes.c_void_p]
+    probe.tv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_void_p]
     probe.tv_probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     probe.tv_probe_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     probe.tv_probe_mfma_loop_flops.restype = ctypes.c_double
@@ -211,9 +211,10 @@ def achievable_peaks(torch, dev, stream):
     nblk = 2048  # the fastest of 512 .. 16384 workgroups on this device
     sink = torch.empty(4096 * 256, dtype=torch.float32, device=dev)
     big = torch.ones((2 << 30) // 4, dtype=torch.float32, device=dev)
-    t = timed(lambda: call(probe.tv_probe_stream_read(ctypes.c_void_p(big.data_ptr()), big.numel() * 4,
-                                                      ctypes.c_void_p(sink.data_ptr()), nblk, st)), 5)
-    out["hbm_read_GB/s"] = round(big.numel() * 4 / t / 1e9, 1)
+    for nt, key in ((0, "hbm_read_GB/s"), (1, "hbm_read_nontemporal_GB/s")):
+        t = timed(lambda: call(probe.tv_probe_stream_read(ctypes.c_void_p(big.data_ptr()), big.numel() * 4, nt,
+                                                          ctypes.c_void_p(sink.data_ptr()), nblk, st)), 5)
+        out[key] = round(big.numel() * 4 / t / 1e9, 1)
     del big
     mblk, iters = 1024, 4096  # four workgroups of four waves per CU
     for rnd, key in ((0, "mfma_loop_bf16_TFLOP/s"), (1, "mfma_loop_bf16_random_TFLOP/s")):
@@ -409,7 +410,7 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
     else:
         roof = {"bound": "hbm", "achieved": round(acc_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(acc_gbs / HBM_PEAK_GBS, 4),
-                "kernel": "tv::spec_accept_kernel<false, true> (tv_spec_accept sampling, one launch)",
+                "kernel": "tv::spec_accept_kernel<false, ...> (tv_spec_accept sampling, one launch)",
                 "algorithmic_bytes": c_bytes, "avg_us": round(per["accept"] * 1e3, 3)}
         roof["traffic"] = counted_traffic(w.name, "spec_accept_kernel<false, true>", ACC_SOURCES)
     rec = {
@@ -546,7 +547,8 @@ def main():
     roof = head["roofline"]
     peaks = achievable_peaks(torch, dev, stream)
     # MFMA work on real data is held to the clock of the random-operand loop
-    reach = peaks["mfma_loop_bf16_random_TFLOP/s"] if roof["unit"] == "TFLOP/s" else peaks["hbm_read_GB/s"]
+    reach = (peaks["mfma_loop_bf16_random_TFLOP/s"] if roof["unit"] == "TFLOP/s" else
+             max(peaks["hbm_read_GB/s"], peaks["hbm_read_nontemporal_GB/s"]))
     roof["frac_of_achievable"] = round(roof["achieved"] / reach, 4)
 
     res = {

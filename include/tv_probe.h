@@ -17,10 +17,11 @@ extern "C" {
 #endif
 
 /* Streaming read of `bytes` (a multiple of 16 is read; `src` 16-byte aligned)
- * by `nblocks` workgroups of 256 threads with 16-byte loads.  Writes one float
- * per thread to out[nblocks * 256] so that the loads are live.  Bytes read per
- * launch: bytes rounded down to 16. */
-int tv_probe_stream_read(const void* src, size_t bytes, float* out, int nblocks, void* stream);
+ * by `nblocks` workgroups of 256 threads with 16-byte loads, ordinary ones or
+ * (nontemporal != 0) ones marked non-temporal.  Writes one float per thread to
+ * out[nblocks * 256] so that the loads are live.  Bytes read per launch: bytes
+ * rounded down to 16. */
+int tv_probe_stream_read(const void* src, size_t bytes, int nontemporal, float* out, int nblocks, void* stream);
 
 /* `nblocks` workgroups of four waves; each wave issues `iters` rounds of four
  * independent v_mfma_f32_32x32x16_bf16 on register operands: constant ones

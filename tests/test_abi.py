@@ -158,15 +158,16 @@ def test_probe_library_exports_its_header(probe):
 
 
 def test_probe_host_checks(probe):
-    probe.tv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                           ctypes.c_void_p]
+    probe.tv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_void_p]
     probe.tv_probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     probe.tv_probe_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     probe.tv_probe_mfma_loop_flops.restype = ctypes.c_double
-    assert probe.tv_probe_stream_read(None, 1 << 20, 16, 8, None) == -1        # null source
-    assert probe.tv_probe_stream_read(16, 8, 16, 8, None) == -1                # fewer than 16 bytes
-    assert probe.tv_probe_stream_read(24, 1 << 20, 16, 8, None) == -1          # misaligned source
-    assert probe.tv_probe_stream_read(16, 1 << 20, 16, 0, None) == -1          # no workgroups
+    for nt in (0, 1):
+        assert probe.tv_probe_stream_read(None, 1 << 20, nt, 16, 8, None) == -1    # null source
+        assert probe.tv_probe_stream_read(16, 8, nt, 16, 8, None) == -1            # fewer than 16 bytes
+        assert probe.tv_probe_stream_read(24, 1 << 20, nt, 16, 8, None) == -1      # misaligned source
+        assert probe.tv_probe_stream_read(16, 1 << 20, nt, 16, 0, None) == -1      # no workgroups
     for rnd in (0, 1):
         assert probe.tv_probe_mfma_loop(0, 8, rnd, 16, None) == -1
         assert probe.tv_probe_mfma_loop(8, 0, rnd, 16, None) == -1

@@ -3,7 +3,9 @@
 // the verification path.
 //  * stream_read: every workgroup reads a contiguous share of a buffer with
 //    16-byte loads, eight in flight per thread, and keeps one sum per thread
-//    (so the loads are live).  Its bytes per second is a streaming-read rate.
+//    (so the loads are live).  Its bytes per second is a streaming-read rate,
+//    with ordinary loads or with loads marked non-temporal (which skip the
+//    caches' retention and stream faster once the data cannot stay cached).
 //  * mfma_loop: every wave runs four independent chains of
 //    v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 multiply-adds each) on register
 //    operands; nothing else in the loop.  Its FLOP/s is the dense bf16 MFMA
@@ -26,11 +28,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kProbeThreads = 256;
 constexpr int kChains = 4;
 
+template <bool NT>
+__device__ __forceinline__ f32x4 load16(const f32x4* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const f32x4* __restrict__ src, size_t n16,
                                                                     float* __restrict__ out) {
     // workgroup b reads the contiguous range [b * per, (b + 1) * per) of
     // 16-byte vectors, 8 * 256 of them (32 KB) per round, eight loads in
-    // flight per thread
+    // flight per thread (marked non-temporal with NT)
     constexpr int kRound = 8 * kProbeThreads;
     const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
     const size_t lo = min(n16, (size_t)blockIdx.x * per), hi = min(n16, lo + per);
@@ -39,11 +50,11 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const f32x4*
     for (; i + 7 * kProbeThreads < hi; i += kRound) {
         f32x4 x[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = src[i + k * kProbeThreads];
+        for (int k = 0; k < 8; ++k) x[k] = load16<NT>(src + i + k * kProbeThreads);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc += x[k];
     }
-    for (; i < hi; i += kProbeThreads) acc += src[i];
+    for (; i < hi; i += kProbeThreads) acc += load16<NT>(src + i);
     out[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
 }
 
@@ -95,10 +106,15 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_loop_kernel(int iters, flo
 
 }  // namespace
 
-extern "C" int tv_probe_stream_read(const void* src, size_t bytes, float* out, int nblocks, void* stream) {
+extern "C" int tv_probe_stream_read(const void* src, size_t bytes, int nontemporal, float* out, int nblocks,
+                                    void* stream) {
     if (!src || !out || nblocks < 1 || bytes < 16 || (uintptr_t)src % 16 != 0) return -1;
-    hipLaunchKernelGGL(stream_read_kernel, dim3(nblocks), dim3(kProbeThreads), 0, (hipStream_t)stream,
-                       static_cast<const f32x4*>(src), bytes / 16, out);
+    if (nontemporal)
+        hipLaunchKernelGGL(stream_read_kernel<true>, dim3(nblocks), dim3(kProbeThreads), 0, (hipStream_t)stream,
+                           static_cast<const f32x4*>(src), bytes / 16, out);
+    else
+        hipLaunchKernelGGL(stream_read_kernel<false>, dim3(nblocks), dim3(kProbeThreads), 0, (hipStream_t)stream,
+                           static_cast<const f32x4*>(src), bytes / 16, out);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
