@@ -12,7 +12,8 @@
 // competing for a CU's bandwidth).  A team of W workgroups owns one sequence
 // at a time; member w owns vocabulary slice w of every logit row.
 //  1. Statistics: each member streams its slice of every row once (coalesced
-//     16-byte loads, prefetched a group ahead; its sixteen waves take rows
+//     16-byte loads, non-temporal when the call's logits exceed twice the
+//     Infinity Cache, prefetched a group ahead; its sixteen waves take rows
 //     from an LDS counter) and publishes the slice max and sum of
 //     exp((x - max)/T) -- or the max and its first index in greedy mode.
 //     The logits the walk tests, q_parent(c)(x_c) and p_c(x_c), are gathered
