@@ -135,6 +135,31 @@ def accept_bytes(w, greedy):
     return w.B * rows * w.V * 4 + w.B * w.N * 4 * 2
 
 
+def walk_bytes(w, parents, acc_len, acc_nodes, team_size):
+    """Row bytes the sampling walk reads after the statistics pass, from the
+    accepted paths (independent siblings): at every node on the path and at
+    the stop node, each rejected child costs one pass over its p row, and the
+    first rejection at a node also reads the node's q row (later passes keep
+    the residual on chip); a walk that ends at a leaf draws from the leaf's q
+    row in one member's slice (V / team_size logits)."""
+    total = 0
+    for b in range(w.B):
+        par = parents[b]
+        kids = [[] for _ in range(w.N)]
+        for i in range(1, w.N):
+            kids[int(par[i])].append(i)
+        path = [int(x) for x in acc_nodes[b, :max(0, int(acc_len[b]))]]
+        visited = [0] + path
+        rows = 0
+        for k, u in enumerate(visited):
+            rej = kids[u].index(path[k]) if k < len(path) else len(kids[u])
+            rows += rej + (1 if rej > 0 else 0)
+        total += rows * w.V * 4
+        if not kids[visited[-1]]:
+            total += (w.V + team_size - 1) // team_size * 4
+    return total
+
+
 def sleep_cycles_per_ms(torch, stream):
     """Shader-clock cycles of torch's spin kernel per millisecond on this device."""
     a = torch.cuda.Event(enable_timing=True)
@@ -379,13 +404,18 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
              "accept": lambda s: copies[s % ncopies]["sample"].accept(),
              "accept_greedy": lambda s: copies[s % ncopies]["greedy"].accept()}
     per = {n: time_batch(fn, args.steps, stream, torch, lead_of(args.steps)) for n, fn in calls.items()}
+    # the walk's row passes on each copy (its outputs after the timed calls), averaged over the copies
+    team_size = tv.accept_plan(w.B, w.N, w.V, False)[0]
+    w_bytes = sum(walk_bytes(w, parents, c["sample"].acc_len.cpu().numpy(), c["sample"].acc_nodes.cpu().numpy(),
+                             team_size) for c in copies) / len(copies)
     del copies
     torch.cuda.synchronize()
 
     nodes = w.B * (w.N - 1)
     a_bytes = attention_bytes(w)
     a_flops = attention_flops(w, parents)
-    c_bytes = accept_bytes(w, False)
+    c_stream = accept_bytes(w, False)
+    c_bytes = c_stream + int(round(w_bytes))
     attn_gbs = a_bytes / (per["attention"] / 1e3) / 1e9
     attn_tflops = a_flops / (per["attention"] / 1e3) / 1e12
     acc_gbs = c_bytes / (per["accept"] / 1e3) / 1e9
@@ -411,7 +441,8 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
         roof = {"bound": "hbm", "achieved": round(acc_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(acc_gbs / HBM_PEAK_GBS, 4),
                 "kernel": "tv::spec_accept_kernel<false, ...> (tv_spec_accept sampling, one launch)",
-                "algorithmic_bytes": c_bytes, "avg_us": round(per["accept"] * 1e3, 3)}
+                "algorithmic_bytes": c_bytes, "stream_bytes": c_stream, "walk_bytes": c_bytes - c_stream,
+                "avg_us": round(per["accept"] * 1e3, 3)}
         roof["traffic"] = counted_traffic(w.name, "spec_accept_kernel<false, true>", ACC_SOURCES)
     rec = {
         "workload": f"{w.name}: {CONFIG_TEXT[w.name]}",
@@ -428,6 +459,8 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
                       "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                       "bound": "mfma" if mfma_bound else "hbm"},
         "accept": {"GB/s": round(acc_gbs, 1), "hbm_frac": round(acc_gbs / HBM_PEAK_GBS, 4),
+                   "walk_bytes": c_bytes - c_stream,
+                   "stream_GB/s": round(c_stream / (per["accept"] / 1e3) / 1e9, 1),
                    "greedy_GB/s": round(accept_bytes(w, True) / (per["accept_greedy"] / 1e3) / 1e9, 1),
                    "greedy_hbm_frac": round(accept_bytes(w, True) / (per["accept_greedy"] / 1e3) / 1e9
                                             / HBM_PEAK_GBS, 4)},
