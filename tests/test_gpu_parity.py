@@ -452,6 +452,32 @@ def test_accept_sampling_sweep_flip_rate():
     assert flips < FLIP_RATE * nodes
 
 
+@pytest.mark.timeout(600)
+def test_accept_large_odd_vocab_streams(tv):
+    """More than twice the Infinity Cache of logits in both modes (the
+    statistics pass then loads them non-temporally) with a vocabulary that is
+    not a multiple of 4 (scalar loads): bit-exact greedy walks, and sampling
+    walks bit-exact on every unflagged sequence."""
+    B, N, V = 64, 40, 60001
+    rng = np.random.default_rng(23)
+    par = np.stack([np.array([-1] + [int(rng.integers(0, i)) for i in range(1, N)]) for _ in range(B)]).astype(np.int32)
+    q = rng.normal(scale=3.0, size=(B, N, V)).astype(np.float32)
+    p = (q[np.arange(B)[:, None], np.maximum(par, 0)] + rng.normal(size=(B, N, V))).astype(np.float32)
+    p[:, 0] = 0
+    draft = p.argmax(axis=2).astype(np.int32)
+    draft[:, 0] = 0
+    assert B * N * V * 4 > 512 * 2 ** 20  # the greedy stream alone is above the threshold
+    qd, pd = torch.from_numpy(q).to(dev()), torch.from_numpy(p).to(dev())
+    dd, pard = torch.from_numpy(draft).to(dev()), torch.from_numpy(par).to(dev())
+    flips = 0
+    for greedy in (True, False):
+        gpu = _accept_gpu(tv, qd, None if greedy else pd, dd, pard, 3, 1.0, greedy)
+        ref = gh.oracle_accept_chunks(q, None if greedy else p, draft, par, 3, 1.0, label="odd vocab",
+                                      greedy=greedy)
+        flips += _compare_walk(gpu, ref, greedy)
+    assert flips <= FLIP_RATE * B * (N - 1) + 1
+
+
 def _topk_sibling_drafts(p, parent):
     """Distinct sibling tokens: the children of node u take the top tokens of
     p row u in child order (EAGLE-style expansion)."""
