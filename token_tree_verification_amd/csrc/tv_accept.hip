@@ -704,6 +704,30 @@ __device__ __forceinline__ int slice_draw(const float* res, int nsl, double tau,
     return tok;
 }
 
+// The first set bit at or above `from` of a kMaxNodes-bit mask (kMaxNodes /
+// 64 words), or `none`.
+__device__ __forceinline__ int first_bit_from(const uint64_t* m, int from, int none) {
+    for (int k = from >> 6; k < kMaxNodes / kWave; ++k) {
+        uint64_t x = m[k];
+        if (k == (from >> 6)) x &= ~0ull << (from & 63);
+        if (x) return k * kWave + __ffsll((unsigned long long)x) - 1;
+    }
+    return none;
+}
+
+// A walk candidate prepared ahead: child c of u, with what its test needs
+// before the exchange's total is known (pfull: its probability in the draft
+// row it was drawn from; px: the probability it is tested against; r: its
+// uniform; rx0: its probability under softmax(q_u / T)) and what a rejection
+// of it needs (invSp: the scale of the residual pass against its row).  The walk tries each node at most once and always in the
+// same state (the same parent and undrawn mass), so a value prepared for node
+// c is the value the walk would compute on reaching c.
+struct WalkCand {
+    double pfull, px, r, rx0;
+    float invSp;
+    int c;
+};
+
 // ---------------------------------------------------------------- the kernel --
 template <bool GREEDY, bool VEC4, bool NT>
 __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) {
@@ -731,6 +755,9 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
     __shared__ int s_rej[GREEDY ? 1 : kMaxNodes];
     __shared__ uint64_t s_bal[kMaxNodes / kWave];
     __shared__ float s_wx[2], s_nwx[2];
+    __shared__ WalkCand s_prep[2];  // walk candidates prepared during an exchange
+    __shared__ int s_fc[GREEDY ? 1 : kMaxNodes];  // first child of each node (nb: none)
+    __shared__ int s_ns[GREEDY ? 1 : kMaxNodes];  // next sibling of each node (nb: none)
     __shared__ double s_oexcl, s_target;
     __shared__ int s_tok, s_owner, s_fallback, s_rowctr, s_nprow, s_last, s_hitw[kWaves], s_lastw[kWaves];
     __shared__ uint64_t s_base;
@@ -761,6 +788,17 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             if (!GREEDY) s_depth[tid] = 0;  // sampling: marks nodes that have children (below)
         }
         if (tid == 0) s_rowctr = 0;  // every wave finished the previous stream (workgroup barriers followed it)
+        // sampling: children masks of the nodes, built in the residual slice's
+        // space (the walk and the final draw of the previous sequence, its only
+        // users, ended behind workgroup barriers); one word per thread
+        uint64_t* const s_kids = reinterpret_cast<uint64_t*>(s_res);
+        if (!GREEDY) {
+            static_assert(kMaxNodes * (kMaxNodes / 64) <= kThreads, "one mask word per thread");
+            static_assert(GREEDY || kMaxNodes * (kMaxNodes / 64) * 2 <= kMaxSlice, "masks fit the slice space");
+            int t = tid;
+            asm volatile("" : "+v"(t));  // formed here, not held across the sequence loop
+            if (t < kMaxNodes * (kMaxNodes / kWave)) s_kids[t] = 0;
+        }
         const bool all_ok = __syncthreads_and(ok) != 0;
         int32_t* out_nodes = a.accepted + (size_t)b * N;
         int32_t* out_toks = a.tokens + (size_t)b * N;
@@ -787,11 +825,20 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
         // ---- the rows to stream: target rows 0..nb-1, then (sampling) the
         // draft rows: 1..nb-1, or without replacement the rows of the nodes
         // that have children ----
+        if (!GREEDY) {
+            int t = tid;
+            asm volatile("" : "+v"(t));  // formed here, not held across the sequence loop
+            if (t >= 1 && t < nb)
+                atomicOr(reinterpret_cast<unsigned long long*>(&s_kids[s_par[t] * (kMaxNodes / kWave) + (t >> 6)]),
+                         1ull << (t & 63));
+        }
         int nrows = nb;
         if (GREEDY) {
             if (tid < nb) s_srow[tid] = tid;
         } else if (!a.wor) {
-            if (tid < 2 * nb - 1) s_srow[tid] = tid < nb ? tid : N + (tid - nb + 1);
+            int t = tid;
+            asm volatile("" : "+v"(t));  // formed here, not held across the sequence loop
+            if (t < 2 * nb - 1) s_srow[t] = t < nb ? t : N + (t - nb + 1);
             nrows = 2 * nb - 1;
         } else {
             // an opaque copy of the thread index: what is derived from it here is
@@ -820,7 +867,16 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             __syncthreads();
             nrows = nb + s_nprow;
         }
-        __syncthreads();  // the row table is complete
+        __syncthreads();  // the row table (and the children masks) is complete
+        if (!GREEDY) {
+            // the walk's links, published by the merge's barriers
+            int t = tid;
+            asm volatile("" : "+v"(t));  // formed here, not held across the sequence loop
+            if (t < nb) {
+                s_fc[t] = first_bit_from(&s_kids[t * (kMaxNodes / kWave)], t + 1, nb);
+                s_ns[t] = t == 0 ? nb : first_bit_from(&s_kids[s_par[t] * (kMaxNodes / kWave)], t + 1, nb);
+            }
+        }
         // gathered logits of the accept tests, in flight during the stream
         float gq = 0.f, gp = 0.f;
         const int gc = tid + 1;
@@ -897,6 +953,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 s_gq[gc] = gq;
                 s_gp[gc] = gp;
             }
+            if (tid < 2) s_prep[tid].c = -1;  // published by the barrier below
             merge_sampling(stats, nrows, s_srow, W, c, s_M, s_S, stag, sync);
             __syncthreads();
             advance_generation(sync, w, gen_done);
@@ -909,30 +966,40 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             bool res_active = false;  // target at u: residual s_res / Z, else softmax(q_u / T)
             double Z = 1.0, wx_cur = 0.0;
             double zrem = 1.0;        // without replacement: draft mass at u not yet drawn
-            int c_cur = 1;
+            // a candidate's values, one expression each (the same code computes
+            // them here and when they are prepared ahead)
+            const auto cand_pfull = [&](int cn, int pr) {
+                return exp_scaled(s_gp[cn], s_M[N + pr], inv_t64, s_tab) / s_S[N + pr];
+            };
+            const auto cand_px = [&](double pf, int cn, int un, double zr) {
+                if (!wor) return pf;
+                // a token already drawn by an earlier sibling has no mass left
+                bool dup = false;
+                for (int j = un + 1; j < cn; ++j) dup = dup || (s_par[j] == un && s_draft[j] == s_draft[cn]);
+                return (dup || !(zr > 0.0)) ? 0.0 : pf / zr;
+            };
+            const auto cand_r = [&](int cn) { return (double)philox_uniform(a.seed, (uint32_t)cn, (uint32_t)b, 0u); };
+            const auto cand_rx0 = [&](int cn, int un) { return exp_scaled(s_gq[cn], s_M[un], inv_t64, s_tab) / s_S[un]; };
+            const auto cand_invSp = [&](int pr, double zr) { return (float)(1.0 / (s_S[N + pr] * zr)); };
+            int c_cur = s_fc[0];  // the next child of u to try (nb: none left)
+            int invSq_u = -1;  // the node invSq belongs to
+            float invSq = 0.f;
             for (;;) {
-                while (c_cur < nb && s_par[c_cur] != u) ++c_cur;
                 if (c_cur >= nb) break;  // every child of u tried, or u is a leaf
                 const int cc = c_cur;
                 const int pr_c = wor ? u : cc;  // the draft row cc was drawn from
-                const double pfull = exp_scaled(s_gp[cc], s_M[N + pr_c], inv_t64, s_tab) / s_S[N + pr_c];
+                const int pk = s_prep[0].c == cc ? 0 : (s_prep[1].c == cc ? 1 : -1);
+                const double pfull = pk >= 0 ? s_prep[pk].pfull : cand_pfull(cc, pr_c);
                 {
-                    const double rx = res_active ? wx_cur / Z
-                                                 : exp_scaled(s_gq[cc], s_M[u], inv_t64, s_tab) / s_S[u];
-                    double px = pfull;
-                    if (wor) {
-                        // a token already drawn by an earlier sibling has no mass left
-                        bool dup = false;
-                        for (int j = u + 1; j < cc; ++j) dup = dup || (s_par[j] == u && s_draft[j] == s_draft[cc]);
-                        px = (dup || !(zrem > 0.0)) ? 0.0 : pfull / zrem;
-                    }
+                    const double rx = res_active ? wx_cur / Z : (pk >= 0 ? s_prep[pk].rx0 : cand_rx0(cc, u));
+                    const double px = pk >= 0 ? s_prep[pk].px : cand_px(pfull, cc, u, zrem);
                     const double acc = px == 0.0 ? 1.0 : fmin(1.0, rx / px);
-                    const double r = (double)philox_uniform(a.seed, (uint32_t)cc, (uint32_t)b, 0u);
+                    const double r = pk >= 0 ? s_prep[pk].r : cand_r(cc);
                     if (r < acc) {
                         if (tid == 0) s_path[len] = cc;
                         ++len;
                         u = cc;
-                        c_cur = u + 1;
+                        c_cur = s_fc[u];
                         res_active = false;
                         Z = 1.0;
                         zrem = 1.0;
@@ -945,14 +1012,16 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 // anyone reads, and its pass always writes them (x2l is in its
                 // slice), so s_wx needs no reset.  Barriers: the two sums (each on
                 // its own array, so no leading barrier) ----
-                int nxt = cc + 1;
-                while (nxt < nb && s_par[nxt] != u) ++nxt;
+                const int nxt = s_ns[cc];
                 const int x2 = nxt < nb ? s_draft[nxt] - s0 : -1;
                 const int x2l = (x2 >= 0 && x2 < nsl) ? x2 : -1;
                 const float Mq = s_M[u];
-                const float invSq = (float)(1.0 / s_S[u]);
+                if (invSq_u != u) {
+                    invSq = (float)(1.0 / s_S[u]);
+                    invSq_u = u;
+                }
                 const float invZ = (float)(1.0 / Z);
-                const float invSp = (float)(1.0 / (s_S[N + pr_c] * zrem));
+                const float invSp = pk >= 0 ? s_prep[pk].invSp : cand_invSp(pr_c, zrem);
                 const float* q_u = qb + (size_t)u * V + s0;
                 const float* p_c = pb + (size_t)pr_c * V + s0;
                 const double part = residual_pass<VEC4>(res_active ? nullptr : q_u, p_c, Mq, invSq, s_M[N + pr_c],
@@ -982,7 +1051,33 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                         s_nwx[1] = __uint_as_float((uint32_t)e[3]);
                     }
                 }
-                const double Znew = block_sum_1b(mt, s_wtw[1]);  // its barrier publishes s_nwx
+                // The last wave takes no part in the polls: while they run it
+                // prepares the next candidate (the next sibling, with the mass
+                // left after this pass) and that sibling's first child (reached
+                // only by accepting the sibling: undrawn mass 1), one per lane.
+                // The barrier of the sum below publishes them.
+                if (tid >= kThreads - kWave) {
+                    const int k = tid - (kThreads - kWave);
+                    if (k < 2) {
+                        const int un = k == 0 ? u : nxt;
+                        const int cn = k == 0 ? nxt : (nxt < nb ? s_fc[nxt] : nb);
+                        if (cn < nb) {
+                            const double zr = k == 0 ? zrem : 1.0;
+                            const int pr = wor ? un : cn;
+                            WalkCand wc;
+                            wc.c = cn;
+                            wc.pfull = cand_pfull(cn, pr);
+                            wc.px = cand_px(wc.pfull, cn, un, zr);
+                            wc.r = cand_r(cn);
+                            wc.rx0 = cand_rx0(cn, un);
+                            wc.invSp = cand_invSp(pr, zr);
+                            s_prep[k] = wc;
+                        } else {
+                            s_prep[k].c = -1;
+                        }
+                    }
+                }
+                const double Znew = block_sum_1b(mt, s_wtw[1]);  // its barrier publishes s_nwx and s_prep
                 ++pass;
                 if (Znew > 0.0) {
                     if (tid < W) s_mass[tid] = mt;
@@ -1008,7 +1103,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                                             s_rejP[k], iz, c, nsl, s_res, -1, &s_wx[1], &s_wx[1]);
                     }
                 }
-                c_cur = cc + 1;
+                c_cur = nxt;
             }
 
             // ---- 5. the extra token: inverse CDF over the slices ----
