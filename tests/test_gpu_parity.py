@@ -759,6 +759,42 @@ def test_dynamic_tree_bit_exact(tv, B, V, topk, depth, M, T):
     assert np.array_equal(_np(anc).view(np.uint64), o_anc) and (o_st == 0).all() and (_np(st) == 0).all()
 
 
+def test_dynamic_tree_at_the_timed_shape(tv):
+    """The expansion step the benchmark times, at its shape and launch (64
+    sequences, 10 frontier rows of vocabulary 128256, top-10, after a root
+    step), then the selection of 64 nodes.  Sequences are independent, so the
+    oracle checks a sample of 8 of them: pool values, parents, tokens, frontier
+    and the selected trees bit-exact."""
+    from oracle import dynamic_tree as dt
+    B, F, K, V, M, T = 64, 10, 10, 128256, 64, 1.0
+    P = 1 + K + 5 * K * K
+    sel = np.array([0, 5, 17, 26, 33, 47, 58, 63])
+    S = len(sel)
+    rng = np.random.default_rng(20251)
+    pool = tv.tree_pool(B, P, dev())
+    o_score = np.full((S, P), -np.inf, np.float32)
+    o_par = np.full((S, P), -1, np.int32)
+    o_tok = np.full((S, P), -1, np.int32)
+    root = (np.arange(B, dtype=np.int32) * 13) % V
+    frontier, o_front, base = None, None, 1
+    for fr in (1, F):
+        logits = (rng.standard_normal((B, fr, V), dtype=np.float32) * 2.0).astype(np.float32)
+        frontier = tv.tree_expand(torch.from_numpy(logits).to(dev()), frontier, pool, base, K, F, T,
+                                  root_token=torch.from_numpy(root).to(dev()) if fr == 1 else None)
+        o_front = dt.expand(logits[sel], o_front, o_score, o_par, o_tok, base, K, F, T, root_token=root[sel])
+        base += fr * K
+        torch.cuda.synchronize()
+        gh.say(f"expansion of {fr} row(s) for {B} sequences, {S} compared")
+        assert np.array_equal(_np(pool[1])[sel], o_par)
+        assert np.array_equal(_np(pool[2])[sel], o_tok)
+        assert np.array_equal(_np(pool[0])[sel].view(np.uint32), o_score.view(np.uint32))
+        assert np.array_equal(_np(frontier)[sel], o_front)
+    par, toks, idx, nodes = tv.tree_select(pool, base, M)
+    o_sel = dt.select(o_score, o_par, o_tok, base, M)
+    for got, want in zip((par, toks, idx, nodes), o_sel):
+        assert np.array_equal(_np(got)[sel], want)
+
+
 def test_graph_replay_matches_eager(tv):
     """The three calls captured in one HIP graph and replayed repeatedly, with
     eager work in between, give the eager results every time (the accept and
