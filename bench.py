@@ -135,8 +135,26 @@ def accept_bytes(w, greedy):
     return w.B * rows * w.V * 4 + w.B * w.N * 4 * 2
 
 
+def family_bytes(w, parents, acc_len, acc_nodes, wor=False):
+    """Row bytes of the sampling call's statistics: every node the walk reaches
+    (the root and each accepted node) streams its family once, its target row
+    and the draft rows its children were drawn from (one row per child, or
+    without replacement the node's own row when it has children)."""
+    import numpy as np
+    total = 0
+    for b in range(w.B):
+        par = parents[b]
+        nkids = np.zeros(w.N, dtype=np.int64)
+        for i in range(1, w.N):
+            nkids[int(par[i])] += 1
+        visited = [0] + [int(x) for x in acc_nodes[b, :max(0, int(acc_len[b]))]]
+        rows = sum(1 + (min(1, int(nkids[u])) if wor else int(nkids[u])) for u in visited)
+        total += rows * w.V * 4
+    return total
+
+
 def walk_bytes(w, parents, acc_len, acc_nodes, team_size):
-    """Row bytes the sampling walk reads after the statistics pass, from the
+    """Row bytes the sampling walk reads beside the statistics, from the
     accepted paths (independent siblings): at every node on the path and at
     the stop node, each rejected child costs one pass over its p row, and the
     first rejection at a node also reads the node's q row (later passes keep
@@ -404,17 +422,21 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
              "accept": lambda s: copies[s % ncopies]["sample"].accept(),
              "accept_greedy": lambda s: copies[s % ncopies]["greedy"].accept()}
     per = {n: time_batch(fn, args.steps, stream, torch, lead_of(args.steps)) for n, fn in calls.items()}
-    # the walk's row passes on each copy (its outputs after the timed calls), averaged over the copies
+    # the rows the sampling call reads on each copy (its outputs after the timed
+    # calls): the families of the nodes its walk reaches and the walk's row
+    # passes, averaged over the copies
     team_size = tv.accept_plan(w.B, w.N, w.V, False)[0]
-    w_bytes = sum(walk_bytes(w, parents, c["sample"].acc_len.cpu().numpy(), c["sample"].acc_nodes.cpu().numpy(),
-                             team_size) for c in copies) / len(copies)
+    outs = [(c["sample"].acc_len.cpu().numpy(), c["sample"].acc_nodes.cpu().numpy()) for c in copies]
+    f_bytes = sum(family_bytes(w, parents, al, an) for al, an in outs) / len(outs)
+    w_bytes = sum(walk_bytes(w, parents, al, an, team_size) for al, an in outs) / len(outs)
     del copies
     torch.cuda.synchronize()
 
     nodes = w.B * (w.N - 1)
     a_bytes = attention_bytes(w)
     a_flops = attention_flops(w, parents)
-    c_stream = accept_bytes(w, False)
+    c_full = accept_bytes(w, False)  # what a pass over every row would read
+    c_stream = int(round(f_bytes)) + w.B * w.N * 4 * 2
     c_bytes = c_stream + int(round(w_bytes))
     attn_gbs = a_bytes / (per["attention"] / 1e3) / 1e9
     attn_tflops = a_flops / (per["attention"] / 1e3) / 1e12
@@ -442,7 +464,7 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
                 "frac": round(acc_gbs / HBM_PEAK_GBS, 4),
                 "kernel": "tv::spec_accept_kernel<false, ...> (tv_spec_accept sampling, one launch)",
                 "algorithmic_bytes": c_bytes, "stream_bytes": c_stream, "walk_bytes": c_bytes - c_stream,
-                "avg_us": round(per["accept"] * 1e3, 3)}
+                "all_rows_bytes": c_full, "avg_us": round(per["accept"] * 1e3, 3)}
         roof["traffic"] = counted_traffic(w.name, "spec_accept_kernel<false, true>", ACC_SOURCES)
     rec = {
         "workload": f"{w.name}: {CONFIG_TEXT[w.name]}",
@@ -459,8 +481,9 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
                       "mfma_frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                       "bound": "mfma" if mfma_bound else "hbm"},
         "accept": {"GB/s": round(acc_gbs, 1), "hbm_frac": round(acc_gbs / HBM_PEAK_GBS, 4),
-                   "walk_bytes": c_bytes - c_stream,
-                   "stream_GB/s": round(c_stream / (per["accept"] / 1e3) / 1e9, 1),
+                   "bytes": c_bytes, "walk_bytes": c_bytes - c_stream, "all_rows_bytes": c_full,
+                   # time of a pass over every row at the HBM peak, over this call's time
+                   "vs_all_rows_at_peak": round(c_full / (HBM_PEAK_GBS * 1e9) / (per["accept"] / 1e3), 3),
                    "greedy_GB/s": round(accept_bytes(w, True) / (per["accept_greedy"] / 1e3) / 1e9, 1),
                    "greedy_hbm_frac": round(accept_bytes(w, True) / (per["accept_greedy"] / 1e3) / 1e9
                                             / HBM_PEAK_GBS, 4)},

@@ -1,6 +1,6 @@
-"""The benchmark's count of the sampling walk's row passes (the bytes it adds
-to the accept call's statistics pass), against a direct re-walk on small
-random trees and against hand-worked cases."""
+"""The benchmark's counts of the rows the sampling call reads -- the families
+of the nodes its walk reaches, and the walk's row passes -- against a direct
+re-walk on small random trees and against hand-worked cases."""
 import numpy as np
 
 import bench
@@ -27,6 +27,20 @@ def test_walk_bytes_hand_cases():
     assert bench.walk_bytes(w, star, np.array([0]), np.array([[-1, -1, -1, -1]]), 4) == 4 * 10 * 4
 
 
+def test_family_bytes_hand_cases():
+    w = _small(1, 4, 10)
+    chain = np.array([[-1, 0, 1, 2]])
+    # root family (q0, p1), node 1's (q1, p2): two nodes reached
+    assert bench.family_bytes(w, chain, np.array([1]), np.array([[1, -1, -1, -1]])) == 4 * 10 * 4
+    # every node reached: three families of two rows and the leaf's target row
+    assert bench.family_bytes(w, chain, np.array([3]), np.array([[1, 2, 3, -1]])) == 7 * 10 * 4
+    star = np.array([[-1, 0, 0, 0]])
+    # the root's family has its three children's draft rows; leaf 3 adds its target row
+    assert bench.family_bytes(w, star, np.array([1]), np.array([[3, -1, -1, -1]])) == 5 * 10 * 4
+    # without replacement the children share the root's draft row
+    assert bench.family_bytes(w, star, np.array([0]), np.array([[-1, -1, -1, -1]]), wor=True) == 2 * 10 * 4
+
+
 def _rewalk(q, p, d, par, seed, T):
     """Rejections and q-row reads of the walk, taken step by step in fp64."""
     N, V = q.shape
@@ -34,10 +48,11 @@ def _rewalk(q, p, d, par, seed, T):
         y = x.astype(np.float64) / T
         e = np.exp(y - y.max())
         return e / e.sum()
-    u, rows, leaf = 0, 0, False
+    u, rows, leaf, fam = 0, 0, False, 0
     R = sm(q[0])
     while True:
         kids = [c for c in range(u + 1, N) if par[c] == u]
+        fam += 1 + len(kids)  # u reached: its target row and its children's draft rows
         if not kids:
             leaf = True
             break
@@ -55,7 +70,7 @@ def _rewalk(q, p, d, par, seed, T):
         rows += rej + (1 if rej else 0)
         if not moved:
             break
-    return rows, leaf
+    return rows, leaf, fam
 
 
 def test_walk_bytes_match_a_rewalk():
@@ -73,9 +88,10 @@ def test_walk_bytes_match_a_rewalk():
         res = oracle.spec_accept(q[None], p[None], d[None], par[None].astype(np.int32), seed=trial, temperature=1.0)
         if res["flags"][0]:
             continue
-        rows, leaf = _rewalk(q, p, d, par, trial, 1.0)
+        rows, leaf, fam = _rewalk(q, p, d, par, trial, 1.0)
         want = rows * V * 4 + ((V + team - 1) // team * 4 if leaf else 0)
         got = bench.walk_bytes(w, par[None], res["accept_len"], res["accepted_nodes"], team)
         assert got == want, (trial, got, want)
+        assert bench.family_bytes(w, par[None], res["accept_len"], res["accepted_nodes"]) == fam * V * 4, trial
         checked += 1
     assert checked >= 50

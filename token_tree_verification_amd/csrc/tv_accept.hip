@@ -11,19 +11,20 @@
 // One launch of one 1024-thread workgroup per CU (no co-resident workgroups
 // competing for a CU's bandwidth).  A team of W workgroups owns one sequence
 // at a time; member w owns vocabulary slice w of every logit row.
-//  1. Statistics: each member streams its slice of every row once (coalesced
-//     16-byte loads, non-temporal when the call's logits exceed twice the
-//     Infinity Cache, prefetched a group ahead; its sixteen waves take rows
-//     from an LDS counter) and publishes the slice max and sum of
-//     exp((x - max)/T) -- or the max and its first index in greedy mode.
-//     The logits the walk tests, q_parent(c)(x_c) and p_c(x_c), are gathered
-//     while the stream is in flight.
+//  1. Statistics: each member streams its slice of a list of rows once
+//     (coalesced 16-byte loads, non-temporal in greedy mode when the call's
+//     logits exceed twice the Infinity Cache, prefetched a group ahead; its sixteen waves
+//     take rows from an LDS counter) and publishes per row the slice max and
+//     sum of exp((x - max)/T) -- or the max and its first index in greedy mode.
 //  2. Greedy: every member merges the argmax of every target row from the
 //     other members' entries; member 0 writes the path.
-//  3. Sampling: every member merges the statistics of
-//     every row and runs the same walk redundantly: decisions need only the
-//     merged statistics and the gathered logits, so all members agree bit for
-//     bit without communicating.
+//  3. Sampling: the walk reads few of the rows (on random trees ~6% of the
+//     logits), so statistics are computed per node as the walk reaches it:
+//     its family, the node's target row and the draft rows its children were
+//     drawn from, is streamed and merged before its children are tested.
+//     Every member runs the same walk redundantly: decisions need only the
+//     merged statistics and the gathered logits q_parent(c)(x_c) and p_c(x_c),
+//     so all members agree bit for bit without communicating.
 //  4. A rejection costs one pass over the slices: the residual
 //     max(0, R - P_c) replaces the member's slice of R in LDS, and its slice
 //     mass and the residual at the next sibling's token are exchanged.
@@ -755,11 +756,11 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
     __shared__ int s_rej[GREEDY ? 1 : kMaxNodes];
     __shared__ uint64_t s_bal[kMaxNodes / kWave];
     __shared__ float s_wx[2], s_nwx[2];
-    __shared__ WalkCand s_prep[2];  // walk candidates prepared during an exchange
+    __shared__ WalkCand s_prep;     // the walk candidate prepared during an exchange
     __shared__ int s_fc[GREEDY ? 1 : kMaxNodes];  // first child of each node (nb: none)
     __shared__ int s_ns[GREEDY ? 1 : kMaxNodes];  // next sibling of each node (nb: none)
     __shared__ double s_oexcl, s_target;
-    __shared__ int s_tok, s_owner, s_fallback, s_rowctr, s_nprow, s_last, s_hitw[kWaves], s_lastw[kWaves];
+    __shared__ int s_tok, s_owner, s_fallback, s_rowctr, s_last, s_hitw[kWaves], s_lastw[kWaves];
     __shared__ uint64_t s_base;
 
     if (tid < 32) exp2_table(s_tab, tid);
@@ -785,7 +786,6 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             s_par[tid] = pr;
             s_draft[tid] = d;
             ok = tid == 0 ? pr == -1 : (pr >= 0 && pr < tid);
-            if (!GREEDY) s_depth[tid] = 0;  // sampling: marks nodes that have children (below)
         }
         if (tid == 0) s_rowctr = 0;  // every wave finished the previous stream (workgroup barriers followed it)
         // sampling: children masks of the nodes, built in the residual slice's
@@ -832,42 +832,11 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 atomicOr(reinterpret_cast<unsigned long long*>(&s_kids[s_par[t] * (kMaxNodes / kWave) + (t >> 6)]),
                          1ull << (t & 63));
         }
-        int nrows = nb;
-        if (GREEDY) {
-            if (tid < nb) s_srow[tid] = tid;
-        } else if (!a.wor) {
-            int t = tid;
-            asm volatile("" : "+v"(t));  // formed here, not held across the sequence loop
-            if (t < 2 * nb - 1) s_srow[t] = t < nb ? t : N + (t - nb + 1);
-            nrows = 2 * nb - 1;
-        } else {
-            // an opaque copy of the thread index: what is derived from it here is
-            // formed here, not held in registers across the sequence loop
-            int t = tid;
-            asm volatile("" : "+v"(t));
-            if (t >= 1 && t < nb) s_depth[s_par[t]] = 1;  // u has a child (same value from every writer)
-            __syncthreads();
-            const bool has = t < nb && s_depth[t] == 1;
-            if (t < kMaxNodes) {
-                const uint64_t bal = __ballot(has);
-                if ((t & (kWave - 1)) == 0) s_bal[t >> 6] = bal;
-            }
-            if (t < nb) s_srow[t] = t;
-            __syncthreads();
-            if (has) {
-                int rank = __popcll(s_bal[t >> 6] & ((1ull << (t & 63)) - 1ull));
-                for (int k = 0; k < (t >> 6); ++k) rank += __popcll(s_bal[k]);
-                s_srow[nb + rank] = N + t;
-            }
-            if (tid == 0) {
-                int tot = 0;
-                for (int k = 0; k < kMaxNodes / kWave; ++k) tot += __popcll(s_bal[k]);
-                s_nprow = tot;
-            }
-            __syncthreads();
-            nrows = nb + s_nprow;
-        }
-        __syncthreads();  // the row table (and the children masks) is complete
+        // greedy: the target rows 0..nb-1 (sampling lists the rows of each
+        // node's family when the walk reaches the node)
+        const int nrows = nb;
+        if (GREEDY && tid < nb) s_srow[tid] = tid;
+        __syncthreads();  // the row table and the children masks are complete
         if (!GREEDY) {
             // the walk's links, published by the merge's barriers
             int t = tid;
@@ -899,8 +868,8 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
         }
         const uint64_t stag = (uint64_t)(gen_tag(sync) | ((uint32_t)iter & 0xfffu)) << 32;
         uint64_t* stats = a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)2 * (GREEDY ? N : 2 * N) * W;
-        stream_slices<GREEDY, VEC4, NT>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag, s_srow);
         if constexpr (GREEDY) {
+            stream_slices<GREEDY, VEC4, NT>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag, s_srow);
             // ---- 2. every member merges (seeing every member's entries), member 0
             // writes the path ----
             int* s_amax = s_path;  // reuse: argmax per target row
@@ -953,14 +922,50 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 s_gq[gc] = gq;
                 s_gp[gc] = gp;
             }
-            if (tid < 2) s_prep[tid].c = -1;  // published by the barrier below
-            merge_sampling(stats, nrows, s_srow, W, c, s_M, s_S, stag, sync);
-            __syncthreads();
-            advance_generation(sync, w, gen_done);
+            if (tid == 0) s_prep.c = -1;  // published by the family's barriers
+            const bool wor = a.wor != 0;
+            // The rows of node un's family: its target row and the draft rows
+            // its children were drawn from (their own rows, or without
+            // replacement un's row), listed in s_srow; returns their number.
+            // Every member lists the same rows in the same order.
+            const auto family = [&](int un) -> int {
+                int t = tid;
+                asm volatile("" : "+v"(t));  // formed here, not held across the sequence loop
+                const bool kid = t >= 1 && t < nb && s_par[t] == un;
+                if (t < kMaxNodes) {
+                    const uint64_t bal = __ballot(kid);
+                    if ((t & (kWave - 1)) == 0) s_bal[t >> 6] = bal;
+                }
+                if (tid == 0) s_rowctr = 0;  // every wave finished the previous stream
+                __syncthreads();
+                int before = 0, total = 0;
+#pragma unroll
+                for (int k = 0; k < kMaxNodes / kWave; ++k) {
+                    const int pc = __popcll(s_bal[k]);
+                    total += pc;
+                    if (k < (t >> 6)) before += pc;
+                }
+                if (kid) before += __popcll(s_bal[t >> 6] & ((1ull << (t & 63)) - 1ull));
+                int nn = N;
+                asm volatile("" : "+s"(nn));  // formed here, not held across the sequence loop
+                if (tid == 0) {
+                    s_srow[0] = un;
+                    if (wor && total > 0) s_srow[1] = nn + un;
+                }
+                if (!wor && kid) s_srow[1 + before] = nn + t;
+                __syncthreads();
+                return 1 + (wor ? (total > 0 ? 1 : 0) : total);
+            };
+            // statistics of node un's family, streamed and merged
+            const auto family_stats = [&](int un) {
+                const int nf = family(un);
+                stream_slices<GREEDY, VEC4, NT>(qb, pb, nf, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag, s_srow);
+                merge_sampling(stats, nf, s_srow, W, c, s_M, s_S, stag, sync);
+                __syncthreads();
+            };
 
             // ---- the walk (identical on every member) ----
             const double inv_t64 = a.inv_t64;
-            const bool wor = a.wor != 0;
             double* massb = a.mass + (size_t)team * N * W * kMassRec;
             int u = 0, len = 0, pass = 0, nrej = 0;
             bool res_active = false;  // target at u: residual s_res / Z, else softmax(q_u / T)
@@ -978,32 +983,45 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 for (int j = un + 1; j < cn; ++j) dup = dup || (s_par[j] == un && s_draft[j] == s_draft[cn]);
                 return (dup || !(zr > 0.0)) ? 0.0 : pf / zr;
             };
-            const auto cand_r = [&](int cn) { return (double)philox_uniform(a.seed, (uint32_t)cn, (uint32_t)b, 0u); };
+            const auto cand_r = [&](int cn) {
+                uint64_t sd = a.seed;
+                asm volatile("" : "+s"(sd));  // the key schedule is formed here, not held across the kernel
+                return (double)philox_uniform(sd, (uint32_t)cn, (uint32_t)b, 0u);
+            };
             const auto cand_rx0 = [&](int cn, int un) { return exp_scaled(s_gq[cn], s_M[un], inv_t64, s_tab) / s_S[un]; };
             const auto cand_invSp = [&](int pr, double zr) { return (float)(1.0 / (s_S[N + pr] * zr)); };
-            int c_cur = s_fc[0];  // the next child of u to try (nb: none left)
+            int c_cur = nb;  // the next child of u to try (nb: none left)
             int invSq_u = -1;  // the node invSq belongs to
             float invSq = 0.f;
+            bool arrived = true;  // at u, whose family's statistics are still to come
             for (;;) {
+                if (arrived) {
+                    // the rows of u's tests (one call site: the stream is inlined
+                    // once); its barriers also publish the tree's links
+                    family_stats(u);
+                    advance_generation(sync, w, gen_done);
+                    c_cur = s_fc[u];
+                    arrived = false;
+                }
                 if (c_cur >= nb) break;  // every child of u tried, or u is a leaf
                 const int cc = c_cur;
                 const int pr_c = wor ? u : cc;  // the draft row cc was drawn from
-                const int pk = s_prep[0].c == cc ? 0 : (s_prep[1].c == cc ? 1 : -1);
-                const double pfull = pk >= 0 ? s_prep[pk].pfull : cand_pfull(cc, pr_c);
+                const bool pk = s_prep.c == cc;
+                const double pfull = pk ? s_prep.pfull : cand_pfull(cc, pr_c);
                 {
-                    const double rx = res_active ? wx_cur / Z : (pk >= 0 ? s_prep[pk].rx0 : cand_rx0(cc, u));
-                    const double px = pk >= 0 ? s_prep[pk].px : cand_px(pfull, cc, u, zrem);
+                    const double rx = res_active ? wx_cur / Z : (pk ? s_prep.rx0 : cand_rx0(cc, u));
+                    const double px = pk ? s_prep.px : cand_px(pfull, cc, u, zrem);
                     const double acc = px == 0.0 ? 1.0 : fmin(1.0, rx / px);
-                    const double r = pk >= 0 ? s_prep[pk].r : cand_r(cc);
+                    const double r = pk ? s_prep.r : cand_r(cc);
                     if (r < acc) {
                         if (tid == 0) s_path[len] = cc;
                         ++len;
                         u = cc;
-                        c_cur = s_fc[u];
                         res_active = false;
                         Z = 1.0;
                         zrem = 1.0;
                         nrej = 0;
+                        arrived = true;
                         continue;
                     }
                 }
@@ -1021,7 +1039,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                     invSq_u = u;
                 }
                 const float invZ = (float)(1.0 / Z);
-                const float invSp = pk >= 0 ? s_prep[pk].invSp : cand_invSp(pr_c, zrem);
+                const float invSp = pk ? s_prep.invSp : cand_invSp(pr_c, zrem);
                 const float* q_u = qb + (size_t)u * V + s0;
                 const float* p_c = pb + (size_t)pr_c * V + s0;
                 const double part = residual_pass<VEC4>(res_active ? nullptr : q_u, p_c, Mq, invSq, s_M[N + pr_c],
@@ -1051,30 +1069,23 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                         s_nwx[1] = __uint_as_float((uint32_t)e[3]);
                     }
                 }
-                // The last wave takes no part in the polls: while they run it
-                // prepares the next candidate (the next sibling, with the mass
-                // left after this pass) and that sibling's first child (reached
-                // only by accepting the sibling: undrawn mass 1), one per lane.
-                // The barrier of the sum below publishes them.
-                if (tid >= kThreads - kWave) {
-                    const int k = tid - (kThreads - kWave);
-                    if (k < 2) {
-                        const int un = k == 0 ? u : nxt;
-                        const int cn = k == 0 ? nxt : (nxt < nb ? s_fc[nxt] : nb);
-                        if (cn < nb) {
-                            const double zr = k == 0 ? zrem : 1.0;
-                            const int pr = wor ? un : cn;
-                            WalkCand wc;
-                            wc.c = cn;
-                            wc.pfull = cand_pfull(cn, pr);
-                            wc.px = cand_px(wc.pfull, cn, un, zr);
-                            wc.r = cand_r(cn);
-                            wc.rx0 = cand_rx0(cn, un);
-                            wc.invSp = cand_invSp(pr, zr);
-                            s_prep[k] = wc;
-                        } else {
-                            s_prep[k].c = -1;
-                        }
+                // The last wave takes no part in the polls: while they run its
+                // first lane prepares the next candidate (the next sibling, with
+                // the mass left after this pass; its row is in u's family).  The
+                // barrier of the sum below publishes it.
+                if (tid == kThreads - kWave) {
+                    if (nxt < nb) {
+                        const int pr = wor ? u : nxt;
+                        WalkCand wc;
+                        wc.c = nxt;
+                        wc.pfull = cand_pfull(nxt, pr);
+                        wc.px = cand_px(wc.pfull, nxt, u, zrem);
+                        wc.r = cand_r(nxt);
+                        wc.rx0 = cand_rx0(nxt, u);
+                        wc.invSp = cand_invSp(pr, zrem);
+                        s_prep = wc;
+                    } else {
+                        s_prep.c = -1;
                     }
                 }
                 const double Znew = block_sum_1b(mt, s_wtw[1]);  // its barrier publishes s_nwx and s_prep
@@ -1107,7 +1118,9 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             }
 
             // ---- 5. the extra token: inverse CDF over the slices ----
-            const double ut = (double)philox_uniform(a.seed, (uint32_t)u, (uint32_t)b, 1u);
+            uint64_t sd = a.seed;
+            asm volatile("" : "+s"(sd));  // the key schedule is formed here, not held across the kernel
+            const double ut = (double)philox_uniform(sd, (uint32_t)u, (uint32_t)b, 1u);
             // slice masses: of the last residual pass, or from the statistics when
             // drawing from softmax(q_u / T)
             double mt = 0.0;
@@ -1371,7 +1384,9 @@ int launch_accept(const float* q_logits, const float* p_logits, const int32_t* d
     // (a plain read of 4 GiB: ~6.8-7.0 TB/s against ~6.1-6.3 with ordinary
     // loads); below twice its size, cached reuse is worth more.
     const double stream_bytes = (double)B * (greedy ? N : 2 * N - 1) * (double)V * 4.0;
-    const bool nt = stream_bytes > kNonTemporalBytes;
+    // (sampling streams only the rows of the nodes the walk reaches, and its
+    // residual passes read them again: its loads keep the lines cached)
+    const bool nt = greedy && stream_bytes > kNonTemporalBytes;
     // The grid never exceeds the resident capacity from the occupancy query, so
     // once earlier work on the stream drains every member is resident and the
     // polls for other members' words make progress (their waits are bounded
