@@ -334,10 +334,15 @@ def test_accept_reuses_workspace_across_calls(tv):
                 ref = oracle.spec_accept(hq, hp, hd, hpar, seed=seed, temperature=1.0, greedy=greedy)
                 _compare_walk((_np(a), _np(n), _np(t)), ref, greedy)
                 calls += 1
-    # team 0's control line: [0] generation (one per call, either mode), [2]
-    # barrier time-out flag
-    ctrl = _np(ws[:128].view(torch.int64))
-    assert ctrl[0] == calls and ctrl[2] == 0
+    # the control words: every team's line holds the generation (one per call,
+    # either mode; the lines past the device's resident workgroups, which no
+    # team reaches, stay zero) in word 0 and in word 2 whether a wait ran out;
+    # past the 1024 lines of 16 words the arrival word, reset by each call's
+    # last workgroup
+    words = _np(ws[:1024 * 16 * 8 + 8].view(torch.int64))
+    gens = words[0:1024 * 16:16]
+    assert gens[0] == calls and set(np.unique(gens).tolist()) <= {0, calls}
+    assert (words[2:1024 * 16:16] == 0).all() and words[1024 * 16] == 0
 
 
 def test_accept_edge_cases(tv):
@@ -363,6 +368,36 @@ def test_accept_edge_cases(tv):
                              torch.zeros((0, 3), dtype=torch.int32, device=dev()),
                              torch.zeros((0, 3), dtype=torch.int32, device=dev()), greedy=True)
     assert a.numel() == 0
+
+
+def test_accept_greedy_level_by_level(tv):
+    """Greedy verification with large rows per member (64 sequences, vocabulary
+    128256: the target rows are streamed one tree level at a time).  Most
+    drafts equal their parent's argmax, so siblings share tokens and the
+    deepest matching path decides; a quarter of the rows hold their maximum
+    twice (the smaller index is the argmax)."""
+    B, N, V = 64, 16, 128256
+    _, _, sl = tv.accept_plan(B, N, V, True)
+    assert N * sl * 4 > 768 * 1024  # the level-by-level mode
+    rng = np.random.default_rng(17)
+    par = np.stack([random_tree(N, 5, 100 + b) for b in range(B)]).astype(np.int32)
+    q = rng.normal(size=(B, N, V)).astype(np.float32)
+    bi, ni = np.arange(B)[:, None], np.arange(N)[None, :]
+    amax = rng.integers(0, V, size=(B, N))
+    other = rng.integers(0, V, size=(B, N))
+    ties = rng.random((B, N)) < 0.25
+    q[bi, ni, amax] = 9.0
+    q[bi, ni, np.where(ties, other, amax)] = 9.0
+    top = np.where(ties, np.minimum(amax, other), amax)  # first index of the maximum
+    match = rng.random((B, N)) < 0.7
+    draft = np.where(match, top[bi, np.maximum(par, 0)], rng.integers(0, V, size=(B, N))).astype(np.int32)
+    draft[:, 0] = 0
+    tq, td, tpar = (torch.from_numpy(x).to(dev()) for x in (q, draft, par))
+    gpu = _accept_gpu(tv, tq, None, td, tpar, 0, 1.0, True)
+    ref = oracle.spec_accept(q, None, draft, par, greedy=True)
+    gh.say(f"greedy accept lengths: mean {ref['accept_len'].mean():.2f}, max {ref['accept_len'].max()}")
+    assert ref["accept_len"].max() >= 3
+    _compare_walk(gpu, ref, True)
 
 
 def test_accept_invalid_trees_between_valid_ones(tv):

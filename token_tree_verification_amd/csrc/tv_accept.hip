@@ -41,16 +41,19 @@
 // carrying a tag (call generation, sequence or step) in their upper half,
 // written with device-scope stores (coherent across XCDs without L2
 // write-back or invalidation); a reader polls the words it needs until they
-// carry the expected tag, so no barrier separates writer and reader.  Member
-// 0 advances the team's generation word once its first merge of a call has
-// seen every member's entries (every member read the word before streaming),
-// so nothing in the workspace needs clearing after it was zero-filled once.
-// The grid never exceeds the device's resident capacity, so all members of a
-// team run together; spins are bounded.  A wait that runs out is counted in
-// the workspace's arrival word; the last workgroup to finish (arrival count)
-// then reports every sequence of the teams concerned as failed
-// (accept_len -2) and moves their generation past every tag the call may have
-// written, so the workspace stays usable.
+// carry the expected tag, so no barrier separates writer and reader.  The
+// generation is one per call: every team's control line holds the same
+// generation word; every workgroup reads its team's when it starts, and once
+// its first merge has seen every member's entries (every member read the word
+// before streaming), member 0 of team t advances line t and the lines of the
+// teams this call does not have (t + k nteams), so every line advances once a
+// call and the next call's tags differ from every tag of this one, whatever
+// its shape.  Nothing in the workspace needs clearing after it was
+// zero-filled once.  The grid never exceeds the device's resident capacity, so all members
+// of a team run together; spins are bounded.  A wait that runs out is counted
+// in the workspace's arrival word; the last workgroup to finish then reports
+// every sequence of the teams concerned as failed (accept_len -2), and the
+// workspace stays usable.
 //
 // Without-replacement siblings (EAGLE explainer, static-tree verification:
 // the children of a node are alternative candidates for the next position,
@@ -82,6 +85,8 @@ constexpr int kMaxSlice = 32768;     // sampling: a member's residual slice live
 constexpr int kMaxSpans = 4095;      // greedy: spans of 256 logits per slice, at most
 constexpr int kSpan = 4 * kWave;     // logits one wave covers with one 16-byte load per lane
 constexpr int kGroup = 4;            // spans per prefetch group (two groups in flight per wave)
+constexpr int kMinChunkSpans = 8;    // a row split over waves: spans per chunk, at least (8 KB)
+constexpr double kGreedyRowsUpFront = 768.0 * 1024;  // greedy: member bytes of every target row, at most, to stream them up front
 constexpr int kCtrlLine = 16;        // u64 words per team: [0] generation, [2] a wait ran out in this call
 constexpr int kTagShift = 24;        // TeamSync::base = generation << kTagShift
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one wait (about a second)
@@ -109,7 +114,9 @@ struct AccArgs {
     uint64_t* stats;     // [nteams][2][2N][W][2] tagged (max), (sum); greedy [nteams][2][N][W][2] (max), (index)
     double* mass;        // sampling: [nteams][N][W][kMassRec]
     int B, N, V, W, slice, nteams;
+    int lines;           // control lines in use: teams never exceed the device's resident workgroups
     int wor;             // siblings drawn without replacement: p row u serves u's children
+    int greedy_rows;     // greedy: every target row's statistics up front (else one tree level at a time)
     uint32_t spin_limit; // polls a wait makes before it gives up
     float c;             // log2(e) / T
     double inv_t64;      // 1 / T
@@ -127,8 +134,10 @@ __device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint
 
 struct TeamSync {
     uint64_t* line;    // this team's control line
+    uint64_t* ctrl;    // every team's control line ([kMaxTeams][kCtrlLine])
+    int team, nteams, lines;
     uint64_t* done;    // the call's arrival word
-    uint64_t base;     // (generation of this call) << kTagShift
+    uint64_t base;     // (generation of this call) << kTagShift: one per call, for every team
     uint32_t limit;    // polls per wait
 };
 
@@ -144,13 +153,15 @@ __device__ __forceinline__ void wait_failed(uint64_t* line, uint64_t* done) {
 
 // Walk steps exchange tagged words: the tag is (1 << 31 | generation mod 2^19
 // << 12 | sequence iteration mod 16 << 8 | rejection pass) in the upper 32
-// bits of every 64-bit word.  A slot is indexed by the pass, and the members
-// of a team are never more than one sequence apart during a walk (each needs
-// every member's statistics of its sequence first), so a word from an earlier
-// sequence or call is told apart (an older call would have to be 2^19 calls
-// back), and the top bit keeps every tag apart from never-written (zero)
-// memory.  Statistics entries use (1 << 31 | generation << 12 | sequence of
-// the team) the same way.
+// bits of every 64-bit word.  The generation is the call's, the same for every
+// team (a workspace reused with another shape puts other teams' words at the
+// same addresses: a generation per team could repeat there).  A slot is
+// indexed by the pass, and the members of a team are never more than one
+// sequence apart during a walk (each needs every member's statistics of its
+// sequence first), so a word from an earlier sequence or call is told apart
+// (an older call would have to be 2^19 calls back), and the top bit keeps
+// every tag apart from never-written (zero) memory.  Statistics entries use
+// (1 << 31 | generation << 12 | sequence of the team) the same way.
 __device__ __forceinline__ uint32_t gen_tag(const TeamSync& s) {
     return 0x80000000u | (((uint32_t)(s.base >> kTagShift) & 0x7ffffu) << 12);
 }
@@ -180,9 +191,15 @@ __device__ __forceinline__ void gather_tagged(const TeamSync& s, const uint64_t*
 
 // After the first merge of a call every member of the team has read the
 // team's generation word (before it streamed): member 0 advances it for the
-// next call.
+// next call, and with it the lines of the teams this call does not have (one
+// store per thread; lines up to the device's resident workgroups, which no
+// team index reaches), so that every line holds the same generation.  Called
+// by every thread of the workgroup.
 __device__ __forceinline__ void advance_generation(const TeamSync& s, int w, bool& done) {
-    if (!done && w == 0 && threadIdx.x == 0) st_dev(&s.line[0], s.base >> kTagShift);
+    if (!done && w == 0) {
+        const int L = s.team + (int)threadIdx.x * s.nteams;
+        if (L < s.lines) st_dev(&s.ctrl[(size_t)L * kCtrlLine], s.base >> kTagShift);
+    }
     done = true;
 }
 
@@ -262,7 +279,7 @@ __device__ __forceinline__ const float* row_ptr(const float* qb, const float* pb
 // span) and the row's slice statistics are published when its last span is
 // processed: sampling (max, sum of exp((x - max) c), accumulated in fp64,
 // stored as fp32), greedy (max, first index).
-template <bool GREEDY, bool VEC4, bool NT>
+template <bool GREEDY, bool VEC4, bool NT, bool CHUNKS>
 __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, int nrows, int N, int V, int s0,
                                               int nsl, float c, uint64_t* stats, int W, int w, int* rowctr,
                                               uint64_t tg, const int* srow) {
@@ -274,12 +291,39 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
         return __builtin_amdgcn_readfirstlane(v);
     };
     static_assert(2 * kMaxNodes <= 1024 && kMaxSpans < 4096, "tag fields");
-    // load cursor: row li (claim index), span lj; past the last row the cursor
-    // stays on its last span and marks the loads as fillers
-    int li = take();
-    int lj = 0;
-    bool lvalid = li < nrows;
-    const float* lrow = row_ptr(qb, pb, srow[lvalid ? li : 0], N, V) + s0;
+    // Fewer rows than waves: each row is cut into ch chunks of spc spans (at
+    // least kMinChunkSpans), so that every wave has work; a chunk's statistics
+    // go to LDS and are combined per row, in chunk order, after the stream.
+    // Waves claim units (row li = unit / ch, chunk unit % ch).
+    int ch = 1, spc = nspan;
+    if constexpr (CHUNKS) {
+        ch = nrows >= kWaves ? 1 : kWaves / nrows;
+        if (ch > nspan / kMinChunkSpans) ch = max(1, nspan / kMinChunkSpans);
+        spc = (nspan + ch - 1) / ch;
+        ch = (nspan + spc - 1) / spc;  // no empty chunk
+    }
+    const int nunits = nrows * ch;
+    __shared__ float s_cm[kWaves];   // per chunk: max (or best value, greedy)
+    __shared__ double s_cs[kWaves];  // sum of exp((x - max)/T)
+    __shared__ int s_ci[kWaves];     // greedy: first index of the best value
+    // load cursor: unit lu, its row li and span lj of [lbeg, lend); past the
+    // last unit the cursor stays on its last span and marks the loads as fillers
+    int lu = take();
+    int li = 0, lj = 0, lbeg = 0, lend = 0;
+    auto start = [&](int u) {
+        if (!CHUNKS || ch == 1) {  // uniform: whole rows
+            li = u;
+            lbeg = lj = 0;
+            lend = nspan;
+        } else {
+            li = u / ch;
+            lbeg = lj = (u % ch) * spc;
+            lend = min(nspan, lbeg + spc);
+        }
+    };
+    bool lvalid = lu < nunits;
+    start(lvalid ? lu : 0);
+    const float* lrow = row_ptr(qb, pb, srow[li], N, V) + s0;
     auto load = [&](f32x4& x, int& xt) {
         const int e = lj * kSpan;
         if constexpr (VEC4) {
@@ -305,17 +349,18 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
                 x[k] = v < nsl ? t : -INFINITY;
             }
         }
-        xt = lvalid ? (li << 12 | lj | (lj == nspan - 1 ? (int)0x80000000 : 0)) : -1;
+        // tag: unit, span, first (bit 30) and last (bit 31) span of the unit
+        xt = lvalid ? (lu << 12 | lj | (lj == lbeg ? 0x40000000 : 0) | (lj == lend - 1 ? (int)0x80000000 : 0)) : -1;
         if (!lvalid) return;
-        if (++lj == nspan) {
+        if (++lj == lend) {
             const int nxt = take();
-            if (nxt < nrows) {
-                li = nxt;
-                lj = 0;
+            if (nxt < nunits) {
+                lu = nxt;
+                start(lu);
                 lrow = row_ptr(qb, pb, srow[li], N, V) + s0;
             } else {
                 lvalid = false;
-                lj = nspan - 1;
+                lj = lend - 1;
             }
         }
     };
@@ -330,7 +375,7 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
             return;
         }
         const int j = tag & 4095;
-        if (j == 0) {
+        if (tag & 0x40000000) {
             m = -INFINITY;
             s = 0.0;
             bv = -INFINITY;
@@ -358,21 +403,33 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
                 s += (double)(e0 + e1);
             }
         }
-        if (tag < 0) {  // the row's last span: reduce over the wave and publish
-            const int r = srow[(tag >> 12) & 1023];
+        if (tag < 0) {  // the unit's last span: reduce over the wave, publish or keep
+            const int u = (tag >> 12) & 0x3ffff;
             if constexpr (GREEDY) {
                 group_argmax_dpp(bv, bi, kWave);
                 if (lane == 0) {
-                    st_dev(&stats[2 * ((size_t)r * W + w)], tg | __float_as_uint(bv));
-                    st_dev(&stats[2 * ((size_t)r * W + w) + 1], tg | (uint32_t)bi);
+                    if (!CHUNKS || ch == 1) {
+                        const int r = srow[u];
+                        st_dev(&stats[2 * ((size_t)r * W + w)], tg | __float_as_uint(bv));
+                        st_dev(&stats[2 * ((size_t)r * W + w) + 1], tg | (uint32_t)bi);
+                    } else {
+                        s_cm[u] = bv;
+                        s_ci[u] = bi;
+                    }
                 }
             } else {
                 const float M = group_max_dpp(m, kWave);
                 const double f = (m == -INFINITY) ? 0.0 : (double)__builtin_amdgcn_exp2f((m - M) * c);
                 const double S = group_sum_dpp(s * f, kWave);
                 if (lane == 0) {
-                    st_dev(&stats[2 * ((size_t)r * W + w)], tg | __float_as_uint(M));
-                    st_dev(&stats[2 * ((size_t)r * W + w) + 1], tg | __float_as_uint((float)S));
+                    if (!CHUNKS || ch == 1) {
+                        const int r = srow[u];
+                        st_dev(&stats[2 * ((size_t)r * W + w)], tg | __float_as_uint(M));
+                        st_dev(&stats[2 * ((size_t)r * W + w) + 1], tg | __float_as_uint((float)S));
+                    } else {
+                        s_cm[u] = M;
+                        s_cs[u] = S;
+                    }
                 }
             }
         }
@@ -395,6 +452,30 @@ __device__ __forceinline__ void stream_slices(const float* qb, const float* pb, 
 #pragma unroll
         for (int i = 0; i < NG; ++i)
             if (!done) process(xb[i], tb[i]);
+    }
+    if (CHUNKS && ch > 1) {  // uniform: a row's chunks, combined in order, then published
+        __syncthreads();
+        const int t = threadIdx.x;
+        if (t < nrows) {
+            const int r = srow[t];
+            if constexpr (GREEDY) {
+                float v = -INFINITY;
+                int i = 0x7fffffff;
+                for (int k = 0; k < ch; ++k) argmax_merge(v, i, s_cm[t * ch + k], s_ci[t * ch + k]);
+                st_dev(&stats[2 * ((size_t)r * W + w)], tg | __float_as_uint(v));
+                st_dev(&stats[2 * ((size_t)r * W + w) + 1], tg | (uint32_t)i);
+            } else {
+                float M = -INFINITY;
+                for (int k = 0; k < ch; ++k) M = fmaxf(M, s_cm[t * ch + k]);
+                double S = 0.0;
+                for (int k = 0; k < ch; ++k) {
+                    const float mk = s_cm[t * ch + k];
+                    if (mk != -INFINITY) S += s_cs[t * ch + k] * (double)__builtin_amdgcn_exp2f((mk - M) * c);
+                }
+                st_dev(&stats[2 * ((size_t)r * W + w)], tg | __float_as_uint(M));
+                st_dev(&stats[2 * ((size_t)r * W + w) + 1], tg | __float_as_uint((float)S));
+            }
+        }
     }
 }
 
@@ -529,42 +610,43 @@ __device__ __forceinline__ void merge_sampling(const uint64_t* stats, int nrows,
         merge_sampling_t<1, kMaxTeamSize / kWave>(stats, nrows, srow, W, c, sM, sS, tg, sync);
 }
 
-// Greedy: argmax of every target row 0..N-1 from the entries [r][W].
+// Greedy: argmax amax[r] of the listed target rows r = srow[0..nrows) from
+// the entries [r][W].
 template <int KB, int PER>
-__device__ __forceinline__ void merge_greedy_t(const uint64_t* stats, int N, int W, int* amax, uint64_t tg,
-                                               const TeamSync& sync) {
+__device__ __forceinline__ void merge_greedy_t(const uint64_t* stats, int nrows, const int* srow, int W, int* amax,
+                                               uint64_t tg, const TeamSync& sync) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lpr = lanes_per_row(W);
     const int rpw = kWave / lpr;
     const int g = lane / lpr, li = lane % lpr;
-    for (int base = 0; base < N; base += KB * kWaves * rpw) {
+    for (int base = 0; base < nrows; base += KB * kWaves * rpw) {
         uint32_t idx[KB][PER];
-        const int nk = entry_indices<KB, PER>(base, wave, rpw, g, li, lpr, N, W, nullptr, idx);
+        const int nk = entry_indices<KB, PER>(base, wave, rpw, g, li, lpr, nrows, W, srow, idx);
         if (nk == 0) break;
         uint64_t e[KB][PER][2];
         poll_entries<KB, PER>(stats, idx, nk, tg, e, sync);
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             if (k >= nk) break;
-            const int r = base + (k * kWaves + wave) * rpw + g;
+            const int ri = base + (k * kWaves + wave) * rpw + g;
             float bv = -INFINITY;
             int bi = 0x7fffffff;
 #pragma unroll
             for (int i = 0; i < PER; ++i)
                 if (li + lpr * i < W) argmax_merge(bv, bi, lo_f(e[k][i][0]), (int)(uint32_t)e[k][i][1]);
             group_argmax_dpp(bv, bi, lpr);
-            if (r < N && li == 0) amax[r] = bi;
+            if (ri < nrows && li == 0) amax[srow[ri]] = bi;
         }
     }
 }
 
-__device__ __forceinline__ void merge_greedy(const uint64_t* stats, int N, int W, int* amax, uint64_t tg,
-                                             const TeamSync& sync) {
+__device__ __forceinline__ void merge_greedy(const uint64_t* stats, int nrows, const int* srow, int W, int* amax,
+                                             uint64_t tg, const TeamSync& sync) {
     if (W <= kWave)
-        merge_greedy_t<4, 1>(stats, N, W, amax, tg, sync);
+        merge_greedy_t<4, 1>(stats, nrows, srow, W, amax, tg, sync);
     else
-        merge_greedy_t<1, kMaxTeamSize / kWave>(stats, N, W, amax, tg, sync);
+        merge_greedy_t<1, kMaxTeamSize / kWave>(stats, nrows, srow, W, amax, tg, sync);
 }
 
 // --------------------------------------------------------- residual passes --
@@ -766,11 +848,17 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
     if (tid < 32) exp2_table(s_tab, tid);
     TeamSync sync;
     sync.line = a.ctrl + (size_t)team * kCtrlLine;
+    sync.ctrl = a.ctrl;
+    sync.team = team;
+    sync.nteams = a.nteams;
+    sync.lines = a.lines;
     sync.done = a.done;
     sync.limit = a.spin_limit;
     sync.base = 0;
-    // this call's tags start above the team's last generation (read before
-    // this member's first arrival; the load overlaps the first tree load)
+    // this call's tags carry the generation after the workspace's last one
+    // (read from the team's own line, before this workgroup's arrival; the
+    // load overlaps the first tree load); the last workgroup to arrive stores
+    // it in every line for the next call
     if (tid == 0) s_base = (ld_dev(&sync.line[0]) + 1) << kTagShift;
     bool have_base = false, gen_done = false;
 
@@ -832,10 +920,12 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
                 atomicOr(reinterpret_cast<unsigned long long*>(&s_kids[s_par[t] * (kMaxNodes / kWave) + (t >> 6)]),
                          1ull << (t & 63));
         }
-        // greedy: the target rows 0..nb-1 (sampling lists the rows of each
-        // node's family when the walk reaches the node)
-        const int nrows = nb;
-        if (GREEDY && tid < nb) s_srow[tid] = tid;
+        if (GREEDY && tid < nb) {
+            // the first rows: every target row, or the root's (s_depth: see below)
+            if (a.greedy_rows) s_srow[tid] = tid;
+            else if (tid == 0) s_srow[0] = 0;
+            s_depth[tid] = tid == 0 ? 1 : 0;
+        }
         __syncthreads();  // the row table and the children masks are complete
         if (!GREEDY) {
             // the walk's links, published by the merge's barriers
@@ -869,51 +959,98 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
         const uint64_t stag = (uint64_t)(gen_tag(sync) | ((uint32_t)iter & 0xfffu)) << 32;
         uint64_t* stats = a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)2 * (GREEDY ? N : 2 * N) * W;
         if constexpr (GREEDY) {
-            stream_slices<GREEDY, VEC4, NT>(qb, pb, nrows, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag, s_srow);
-            // ---- 2. every member merges (seeing every member's entries), member 0
-            // writes the path ----
+            // ---- 2. the end node: the deepest node whose path matches (every
+            // node's draft equals its parent's argmax), ties to the smallest
+            // index.  Small rows: every target row's argmax up front, then each
+            // node checks its own path (s_depth[t]: node t matches).  Large
+            // rows: breadth-first, each level's target rows streamed and merged
+            // as it is reached (level 0 is the root, level k + 1 the matching
+            // children of level-k nodes; s_depth[t]: level of t + 1 on a
+            // matching path, else 0; s_srow: the level's nodes in index order),
+            // and the end node is the first node of the last level ----
             int* s_amax = s_path;  // reuse: argmax per target row
-            merge_greedy(stats, nb, W, s_amax, stag, sync);
-            __syncthreads();
-            advance_generation(sync, w, gen_done);
-            if (w != 0) continue;
-            for (int i = tid; i < N; i += kThreads) {
-                out_nodes[i] = -1;
-                out_toks[i] = -1;
-            }
-            // match(i): node i's draft equals its parent's argmax; valid(i): every
-            // node on the root-to-i path matches.  The end node is the deepest
-            // valid node, ties to the smallest index.
-            if (tid < nb) s_depth[tid] = tid == 0 ? 1 : (s_draft[tid] == s_amax[s_par[tid]]);
-            __syncthreads();
-            float key = -1.f;
-            int kidx = tid;
-            if (tid < nb) {
-                int d = 0;
-                bool v = true;
-                for (int j = tid; j != 0; j = s_par[j]) {
-                    v = v && s_depth[j] != 0;
-                    ++d;
+            const bool all_rows = a.greedy_rows != 0;
+            int lvl = 0, nl = 1, e = 0;
+            for (;;) {
+                if (lvl == 0 || !all_rows) {  // uniform: one stream and merge site for both forms
+                    const int nr = all_rows ? nb : nl;
+                    stream_slices<GREEDY, VEC4, NT, true>(qb, pb, nr, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag,
+                                                          s_srow);
+                    merge_greedy(stats, nr, s_srow, W, s_amax, stag, sync);
+                    __syncthreads();
+                    advance_generation(sync, w, gen_done);
                 }
-                key = v ? (float)d : -1.f;
-            }
-            group_argmax_dpp(key, kidx, kWave);
-            if ((tid & (kWave - 1)) == 0) {
-                s_hitw[tid >> 6] = kidx;
-                s_wt[tid >> 6] = key;
-            }
-            __syncthreads();
-            if (tid == 0) {
-                float bk = s_wt[0];
-                int e = s_hitw[0];
-                for (int k = 1; k < kWaves; ++k) argmax_merge(bk, e, (float)s_wt[k], s_hitw[k]);
-                const int len = (int)bk;
-                for (int i = e, k = len - 1; i != 0; i = s_par[i], --k) {
-                    out_nodes[k] = i;
-                    out_toks[k] = s_draft[i];
+                if (all_rows) {
+                    // every node checks its own path (s_depth[t]: node t matches);
+                    // member 0 alone, which writes the path
+                    if (w != 0) break;
+                    if (tid < nb) s_depth[tid] = tid == 0 ? 1 : (s_draft[tid] == s_amax[s_par[tid]]);
+                    __syncthreads();
+                    float key = -1.f;
+                    int kidx = tid;
+                    if (tid < nb) {
+                        int d = 0;
+                        bool v = true;
+                        for (int j = tid; j != 0; j = s_par[j]) {
+                            v = v && s_depth[j] != 0;
+                            ++d;
+                        }
+                        key = v ? (float)d : -1.f;
+                    }
+                    group_argmax_dpp(key, kidx, kWave);
+                    if ((tid & (kWave - 1)) == 0) {
+                        s_hitw[tid >> 6] = kidx;
+                        s_wt[tid >> 6] = key;
+                    }
+                    __syncthreads();
+                    float bk = s_wt[0];
+                    e = s_hitw[0];
+                    for (int k = 1; k < kWaves; ++k) argmax_merge(bk, e, (float)s_wt[k], s_hitw[k]);
+                    lvl = (int)bk;
+                    break;
                 }
-                out_toks[len] = s_amax[e];
-                __hip_atomic_store(&a.accept_len[b], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // the next level: the matching children of this level's nodes
+                e = s_srow[0];
+                int t = tid;
+                asm volatile("" : "+v"(t));  // formed here, not held across the sequence loop
+                const bool next = t >= 1 && t < nb && s_depth[s_par[t]] == lvl + 1 && s_draft[t] == s_amax[s_par[t]];
+                if (t < kMaxNodes) {
+                    const uint64_t bal = __ballot(next);
+                    if ((t & (kWave - 1)) == 0) s_bal[t >> 6] = bal;
+                }
+                if (tid == 0) s_rowctr = 0;  // every wave finished the stream (the merge's barrier)
+                __syncthreads();  // every read of s_srow, s_depth and s_bal's old words is done
+                int before = 0, total = 0;
+#pragma unroll
+                for (int k = 0; k < kMaxNodes / kWave; ++k) {
+                    const int pc = __popcll(s_bal[k]);
+                    total += pc;
+                    if (k < (t >> 6)) before += pc;
+                }
+                if (total == 0) break;  // uniform
+                if (next) {
+                    s_depth[t] = lvl + 2;
+                    s_srow[before + __popcll(s_bal[t >> 6] & ((1ull << (t & 63)) - 1ull))] = t;
+                }
+                ++lvl;
+                nl = total;
+                __syncthreads();  // the next level's list
+            }
+            if (w != 0) continue;  // member 0 writes the path
+            // member 0 writes the path to e and the extra token, e's argmax
+            if (w == 0) {
+                for (int i = tid; i < N; i += kThreads) {
+                    if (i >= lvl) out_nodes[i] = -1;
+                    if (i > lvl) out_toks[i] = -1;
+                }
+                if (tid == 0) {
+                    for (int i = e, k = lvl - 1; i != 0; i = s_par[i], --k) {
+                        out_nodes[k] = i;
+                        out_toks[k] = s_draft[i];
+                    }
+                    out_toks[lvl] = s_amax[e];
+                    __hip_atomic_store(&a.accept_len[b], lvl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
             __syncthreads();
         } else {
@@ -959,7 +1096,8 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             // statistics of node un's family, streamed and merged
             const auto family_stats = [&](int un) {
                 const int nf = family(un);
-                stream_slices<GREEDY, VEC4, NT>(qb, pb, nf, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag, s_srow);
+                stream_slices<GREEDY, VEC4, NT, true>(qb, pb, nf, N, V, s0, nsl, c, stats, W, w, &s_rowctr, stag,
+                                                      s_srow);
                 merge_sampling(stats, nf, s_srow, W, c, s_M, s_S, stag, sync);
                 __syncthreads();
             };
@@ -1233,12 +1371,13 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             if (ld_dev(&line[2]) == 0) continue;
             for (int bb = t; bb < a.B; bb += a.nteams)
                 __hip_atomic_store(&a.accept_len[bb], -2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // members may have tagged words with this call's generation or the
-            // next one (a member that read the word after member 0 advanced it):
-            // the next call starts past both
-            st_dev(&line[0], ld_dev(&line[0]) + 2);
             st_dev(&line[2], 0ull);
         }
+        // members may have tagged words with this call's generation or the
+        // next one (a member that read its line after member 0 advanced it):
+        // every line moves past both
+        const uint64_t gen = s_base >> kTagShift;
+        for (int t = tid; t < a.lines; t += kThreads) st_dev(&a.ctrl[(size_t)t * kCtrlLine], gen + 1);
     }
 }
 
@@ -1373,7 +1512,11 @@ int launch_accept(const float* q_logits, const float* p_logits, const int32_t* d
     a.W = pl.W;
     a.slice = pl.slice;
     a.nteams = pl.nteams;
+    a.lines = min(resident_capacity(), kMaxTeams);  // every plan's teams fit (nteams <= capacity / W)
     a.wor = (!greedy && (flags & TV_ACCEPT_SIBLINGS_WOR)) ? 1 : 0;
+    // greedy: a member's share of every target row up front when it is small
+    // (its stream costs less than the round trips of a walk level by level)
+    a.greedy_rows = (double)N * pl.slice * 4.0 <= kGreedyRowsUpFront ? 1 : 0;
     a.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
     a.c = greedy ? 1.f : (float)(1.4426950408889634 / (double)temperature);
     a.inv_t64 = greedy ? 1.0 : 1.0 / (double)temperature;
