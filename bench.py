@@ -153,6 +153,22 @@ def family_bytes(w, parents, acc_len, acc_nodes, wor=False):
     return total
 
 
+def greedy_bytes(w, parents, draft, q_argmax):
+    """Row bytes of the greedy call's statistics as a level-by-level search
+    reads them: the root's target row and the target row of every node whose
+    path matches (each draft token on it equals its parent's target argmax)."""
+    import numpy as np
+    total = 0
+    for b in range(w.B):
+        par = parents[b]
+        match = np.zeros(w.N, dtype=bool)
+        match[0] = True
+        for i in range(1, w.N):  # parent[i] < i
+            match[i] = match[int(par[i])] and int(draft[b, i]) == int(q_argmax[b, int(par[i])])
+        total += int(match.sum()) * w.V * 4
+    return total
+
+
 def walk_bytes(w, parents, acc_len, acc_nodes, team_size):
     """Row bytes the sampling walk reads beside the statistics, from the
     accepted paths (independent siblings): at every node on the path and at
@@ -429,6 +445,9 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
     outs = [(c["sample"].acc_len.cpu().numpy(), c["sample"].acc_nodes.cpu().numpy()) for c in copies]
     f_bytes = sum(family_bytes(w, parents, al, an) for al, an in outs) / len(outs)
     w_bytes = sum(walk_bytes(w, parents, al, an, team_size) for al, an in outs) / len(outs)
+    # the greedy call's rows: the matching levels of each copy's trees
+    g_rows = sum(greedy_bytes(w, parents, c["greedy"].keep[7].cpu().numpy(),
+                              c["greedy"].keep[5].argmax(dim=-1).cpu().numpy()) for c in copies) / len(copies)
     del copies
     torch.cuda.synchronize()
 
@@ -438,6 +457,7 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
     c_full = accept_bytes(w, False)  # what a pass over every row would read
     c_stream = int(round(f_bytes)) + w.B * w.N * 4 * 2
     c_bytes = c_stream + int(round(w_bytes))
+    g_bytes = int(round(g_rows)) + w.B * w.N * 4 * 2
     attn_gbs = a_bytes / (per["attention"] / 1e3) / 1e9
     attn_tflops = a_flops / (per["attention"] / 1e3) / 1e12
     acc_gbs = c_bytes / (per["accept"] / 1e3) / 1e9
@@ -484,9 +504,11 @@ def measure(name, args, tv, torch, dev, stream, lead_of, headline):
                    "bytes": c_bytes, "walk_bytes": c_bytes - c_stream, "all_rows_bytes": c_full,
                    # time of a pass over every row at the HBM peak, over this call's time
                    "vs_all_rows_at_peak": round(c_full / (HBM_PEAK_GBS * 1e9) / (per["accept"] / 1e3), 3),
-                   "greedy_GB/s": round(accept_bytes(w, True) / (per["accept_greedy"] / 1e3) / 1e9, 1),
-                   "greedy_hbm_frac": round(accept_bytes(w, True) / (per["accept_greedy"] / 1e3) / 1e9
-                                            / HBM_PEAK_GBS, 4)},
+                   "greedy_bytes": g_bytes, "greedy_all_rows_bytes": accept_bytes(w, True),
+                   "greedy_GB/s": round(g_bytes / (per["accept_greedy"] / 1e3) / 1e9, 1),
+                   "greedy_hbm_frac": round(g_bytes / (per["accept_greedy"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "greedy_vs_all_rows_at_peak": round(accept_bytes(w, True) / (HBM_PEAK_GBS * 1e9)
+                                                       / (per["accept_greedy"] / 1e3), 3)},
         "greedy": {"value": round(nodes / (ms_greedy / 1e3), 1), "ms_per_step": round(ms_greedy, 5)},
         "temperature": T,
     }

@@ -95,3 +95,37 @@ def test_walk_bytes_match_a_rewalk():
         assert bench.family_bytes(w, par[None], res["accept_len"], res["accepted_nodes"]) == fam * V * 4, trial
         checked += 1
     assert checked >= 50
+
+
+def test_greedy_bytes_hand_cases():
+    w = _small(1, 4, 10)
+    star = np.array([[-1, 0, 0, 0]])
+    # the root's argmax is token 5: only child 2 matches, so two target rows
+    assert bench.greedy_bytes(w, star, np.array([[0, 1, 5, 7]]), np.array([[5, 0, 0, 0]])) == 2 * 10 * 4
+    chain = np.array([[-1, 0, 1, 2]])
+    # node 2 does not match, so node 3 below it is never reached although its token matches
+    assert bench.greedy_bytes(w, chain, np.array([[0, 3, 9, 2]]), np.array([[3, 4, 2, 0]])) == 2 * 10 * 4
+    # nothing matches: the root's row alone
+    assert bench.greedy_bytes(w, chain, np.array([[0, 1, 1, 1]]), np.array([[0, 0, 0, 0]])) == 10 * 4
+
+
+def test_greedy_bytes_reach_the_greedy_end():
+    """The deepest node the count includes is as deep as the greedy path."""
+    rng = np.random.default_rng(5)
+    V, N = 6, 14
+    w = _small(1, N, V)
+    for trial in range(40):
+        par = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, N)])
+        q = rng.normal(0, 1.0, (N, V)).astype(np.float32)
+        am = q.argmax(axis=1)
+        d = np.where(rng.random(N) < 0.6, am[np.maximum(par, 0)], rng.integers(0, V, N)).astype(np.int32)
+        d[0] = 0
+        res = oracle.spec_accept(q[None], None, d[None], par[None].astype(np.int32), greedy=True)
+        depth = np.zeros(N, dtype=np.int64)
+        match = np.zeros(N, dtype=bool)
+        match[0] = True
+        for i in range(1, N):
+            depth[i] = depth[par[i]] + 1
+            match[i] = match[par[i]] and d[i] == am[par[i]]
+        assert int(res["accept_len"][0]) == int(depth[match].max()), trial
+        assert bench.greedy_bytes(w, par[None], d[None], am[None]) == int(match.sum()) * V * 4

@@ -16,8 +16,12 @@
 //     logits exceed twice the Infinity Cache, prefetched a group ahead; its sixteen waves
 //     take rows from an LDS counter) and publishes per row the slice max and
 //     sum of exp((x - max)/T) -- or the max and its first index in greedy mode.
-//  2. Greedy: every member merges the argmax of every target row from the
-//     other members' entries; member 0 writes the path.
+//  2. Greedy: every member merges the argmax of target rows from the other
+//     members' entries; member 0 writes the path.  When a member's share of
+//     every target row is small (768 KB at most) all rows are streamed up
+//     front and the deepest matching node is found with one ancestor chase
+//     per node; otherwise the tree is searched one level at a time, streaming
+//     only the rows of the nodes whose path has matched so far.
 //  3. Sampling: the walk reads few of the rows (on random trees ~6% of the
 //     logits), so statistics are computed per node as the walk reaches it:
 //     its family, the node's target row and the draft rows its children were
