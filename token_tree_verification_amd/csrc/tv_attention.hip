@@ -847,7 +847,11 @@ __device__ __forceinline__ uint32_t pack_f16(float x, float y) {
 // barrier per tile: tile t starts by issuing the DMA of tile t+3 (into the
 // stage of tile t-2, last read in block 2t-3 and consumed before the previous
 // barrier) and ends by waiting for the DMA of tile t+2 and converting it;
-// the barrier then publishes tile t+2, first read in block 2t+2.
+// the barrier then publishes tile t+2, first read in block 2t+2.  Full cache
+// tiles are copied from source pointers that advance by one tile per
+// iteration, and the stage addresses of tiles t .. t+4 rotate through scalar
+// registers, so the loop recomputes neither (fewer scalar instructions per
+// tile: c4 ~2-3% faster, outputs bit-identical).
 template <int S, bool NT>
 __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs a) {
     constexpr int NW = 8;
@@ -967,8 +971,8 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
     const uint32_t conv_src = (uint32_t)(TILE + (r0 + ((lane & 15) >> 2)) * kRowBytes +
                                          (((2 * (lane >> 4) + ((lane & 3) >> 1)) ^ (4 * ((lane & 15) >> 2))) << 4) +
                                          8 * (lane & 1));
-    auto convert = [&](int u, int roff) {
-        uint32_t sb = stage(u) + roff * kRowBytes;
+    auto convert_at = [&](uint32_t st, int roff) {
+        uint32_t sb = st + roff * kRowBytes;
         asm volatile("" : "+v"(sb));
         u32x2 part[2][2];  // [dims half][rows part]
 #pragma unroll
@@ -988,6 +992,16 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
                 w[e] = f32x2_to_f16x2_sat(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
             }
             *(lds_u32x4*)(uintptr_t)(sb + TILE + (r0 + 8 * hh) * kRowBytes + lane * 16) = w;
+        }
+    };
+    auto convert = [&](int u, int roff) { convert_at(stage(u), roff); };
+    // DMA of a full cache tile from running source pointers into stage st
+    auto dma_full = [&](const char* kp, const char* vp, uint32_t st, int roff) {
+        const uint32_t dst = st + (r0 + roff) * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            dma16s<NT>(kp + roff * kRowBytes, dk[i], dst + 8 * i * kRowBytes);
+            dma16s<NT>(vp + roff * kRowBytes, dv[i], dst + TILE + 8 * i * kRowBytes);
         }
     };
 
@@ -1021,12 +1035,12 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
 
     // block j = 2t + kb of tile t.  V(j)^T is block kb of tile t; K(j+2) is
     // block kb of tile t+1.
-    auto block = [&](bool masked, int t, int kb) {
+    auto block = [&](bool masked, int t, int kb, uint32_t st0, uint32_t st1) {
         // (opaque to the compiler, so that the constant parts of the
         // addresses fold into the instructions' offsets instead of being
         // precomputed into registers outside the loop)
-        uint32_t sv = stage(t) + 8192 * kb + vt_lane;
-        uint32_t ka = stage(t + 1) + 8192 * kb + k_off;
+        uint32_t sv = st0 + 8192 * kb + vt_lane;
+        uint32_t ka = st1 + 8192 * kb + k_off;
         asm volatile("" : "+v"(sv), "+v"(ka));
         auto pv = [&](int s) {
             const int h = s >> 2, q = s & 3;
@@ -1157,20 +1171,42 @@ __global__ __launch_bounds__(512) void tree_attention_wide_kernel(const AttnArgs
             for (int blk = 0; blk < 4; ++blk) vf[h][blk] = u32x4{0, 0, 0, 0};
 
         const int n_full = (t_begin + n_cache) * KT <= lb ? n_cache : n_cache - 1;
+        // full cache tiles (the DMA's fast path): u < n_dfull
+        const int n_dfull = max(0, min(n_cache, lb / KT - t_begin));
+        // stage addresses of tiles t .. t+4 (t+4 is tile t-1's), rotated per tile
+        uint32_t sr0 = ring_addr, sr1 = ring_addr + STAGE, sr2 = ring_addr + 2 * STAGE, sr3 = ring_addr + 3 * STAGE,
+                 sr4 = ring_addr + 4 * STAGE;
+        // sources of tile t+3 when it is a full cache tile
+        const char* kp = reinterpret_cast<const char*>(kc_p + ((size_t)bg * a.L + (size_t)(t_begin + 3) * KT) * HD);
+        const char* vp = reinterpret_cast<const char*>(vc_p + ((size_t)bg * a.L + (size_t)(t_begin + 3) * KT) * HD);
         for (int t = 0; t < nt; ++t) {
             const bool masked = t >= n_full;  // tree tiles and a ragged last cache tile
+            asm volatile("" : "+s"(kp), "+s"(vp), "+s"(sr0), "+s"(sr1), "+s"(sr2), "+s"(sr3), "+s"(sr4));
             if (wave < 4) {
-                issue_dma(t + 3, 0);
-                issue_dma(t + 3, 32);
+                if (t + 3 < n_dfull) {
+                    dma_full(kp, vp, sr3, 0);
+                    dma_full(kp, vp, sr3, 32);
+                } else {
+                    issue_dma(t + 3, 0);
+                    issue_dma(t + 3, 32);
+                }
             }
-            block(masked, t, 0);
-            block(masked, t, 1);
+            kp += TILE;
+            vp += TILE;
+            block(masked, t, 0, sr0, sr1);
+            block(masked, t, 1, sr0, sr1);
             wait_vmcnt<8>();  // tile t+2 has landed (tile t+3 still in flight)
             if (wave < 4) {
-                convert(t + 2, 0);
-                convert(t + 2, 32);
+                convert_at(sr2, 0);
+                convert_at(sr2, 32);
             }
             __syncthreads();  // tile t+2 is visible; tile t-1's last reads are consumed
+            const uint32_t sfree = sr0;
+            sr0 = sr1;
+            sr1 = sr2;
+            sr2 = sr3;
+            sr3 = sr4;
+            sr4 = sfree;
         }
         // the last block's P.V
 #pragma unroll
