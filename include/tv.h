@@ -238,7 +238,7 @@ int tv_spec_accept_plan(int B, int N, int V, int greedy, int* team_size, int* te
  * TV_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, held until the process ends; it
  * covers every plan of trees up to 64 nodes, and of larger trees with few
  * enough sequences (256-node trees in sampling mode with 256 sequences need
- * 6.1 MiB and are refused); the first
+ * 8.1 MiB and are refused); the first
  * call on a device zeroes its control words with a small kernel on `stream`.
  * Shapes whose plan (tv_spec_accept_workspace) needs more return
  * TV_ERR_SCRATCH before anything is enqueued.  Every call on one GPU shares

@@ -654,6 +654,50 @@ def test_accept_many_sequences_per_team(tv):
     assert (gpu[0] == 0).mean() > 0.5  # the drafts are mostly rejected
 
 
+@pytest.mark.timeout(600)
+def test_accept_exchange_slots_untouched_for_sixteen_sequences(tv):
+    """Two-member teams, 33 sequences each.  The sequences at team iterations
+    0, 16 and 32 are star trees whose children are nearly all rejected (one
+    exchange per rejection); every other sequence is a chain whose drafts the
+    target accepts for certain (draft row = target row, so no exchange at
+    all).  An exchange slot written at iteration 0 is therefore untouched
+    until iteration 16 polls it (and iteration 16's until iteration 32): a
+    record left from sixteen sequences earlier must never pass for the
+    current one."""
+    N, V = 8, 32772
+    W, teams, _ = tv.accept_plan(1 << 20, N, V, False)
+    assert W == 2
+    iters = 33
+    B = teams * iters
+    deep = (np.arange(B) // teams) % 16 == 0
+    star = np.array([-1] + [0] * (N - 1), np.int32)
+    par = np.where(deep[:, None], star[None, :], chain(N)[None, :]).astype(np.int32)
+    g = torch.Generator(device=dev())
+    # sharp target rows on the chains: their final draws then rarely come near
+    # a CDF boundary (flagged draws are counted against the flip budget)
+    sig = torch.from_numpy(np.where(deep, 2.0, 6.0).astype(np.float32)).to(dev())[:, None, None]
+    q = torch.randn((B, N, V), generator=g.manual_seed(11), device=dev()) * sig
+    tpar = torch.from_numpy(par).to(dev())
+    # deep sequences: unrelated draft rows (their argmax is rarely the target's
+    # choice); chains: each draft row is its parent's target row (ratio 1)
+    p = torch.randn((B, N, V), generator=g.manual_seed(12), device=dev()) * 2.0
+    chains = torch.from_numpy(~deep).to(dev())
+    p[chains] = q[chains].index_select(1, torch.from_numpy(np.maximum(chain(N), 0)).long().to(dev()))
+    draft = p.argmax(-1).to(torch.int32)
+    draft[:, 0] = 0
+    a, n, t = tv.spec_accept(q, p, draft, tpar, seed=5, temperature=1.0)
+    torch.cuda.synchronize()
+    gpu = (_np(a), _np(n), _np(t))
+    qn, pn, dn = _np(q), _np(p), _np(draft)
+    del q, p
+    ref = gh.oracle_accept_chunks(qn, pn, dn, par, 5, 1.0, chunk=64, label="stale-slots")
+    assert (gpu[0] >= 0).all(), "a team wait gave up"
+    flips = _compare_walk(gpu, ref, False)
+    assert flips <= FLIP_RATE * B * (N - 1) + 1e-9
+    assert (ref["accept_len"][~deep] == N - 1).all()  # the chains write no exchange record
+    assert (ref["accept_len"][deep] == 0).mean() > 0.5  # the stars mostly reject every child
+
+
 def test_accept_failed_waits_are_reported(tv):
     """A wait that gives up is reported: with the wait limit at 0 every team
     wait gives up at once, every sequence reports accept_len -2 and every

@@ -68,7 +68,7 @@ def test_noalloc_matches_workspace_call(lib):
 
 
 def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
-    """256 sequences of 256-node trees in sampling mode plan 6.1 MiB of team
+    """256 sequences of 256-node trees in sampling mode plan 8.1 MiB of team
     statistics and walk records, more than the 4 MiB scratch: refused before
     anything is enqueued; the same shape in greedy mode fits and runs."""
     import token_tree_verification_amd as tv

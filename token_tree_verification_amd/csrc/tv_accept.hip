@@ -116,7 +116,7 @@ struct AccArgs {
     uint64_t* ctrl;      // [kMaxTeams][kCtrlLine]
     uint64_t* done;      // arrivals of this call (low half), waits that ran out (high half)
     uint64_t* stats;     // [nteams][2][2N][W][2] tagged (max), (sum); greedy [nteams][2][N][W][2] (max), (index)
-    double* mass;        // sampling: [nteams][N][W][kMassRec]
+    double* mass;        // sampling: [nteams][2][N][W][kMassRec] (per team, two sequence buffers)
     int B, N, V, W, slice, nteams;
     int lines;           // control lines in use: teams never exceed the device's resident workgroups
     int wor;             // siblings drawn without replacement: p row u serves u's children
@@ -157,15 +157,24 @@ __device__ __forceinline__ void wait_failed(uint64_t* line, uint64_t* done) {
 
 // Walk steps exchange tagged words: the tag is (1 << 31 | generation mod 2^19
 // << 12 | sequence iteration mod 16 << 8 | rejection pass) in the upper 32
-// bits of every 64-bit word.  The generation is the call's, the same for every
-// team (a workspace reused with another shape puts other teams' words at the
-// same addresses: a generation per team could repeat there).  A slot is
-// indexed by the pass, and the members of a team are never more than one
-// sequence apart during a walk (each needs every member's statistics of its
-// sequence first), so a word from an earlier sequence or call is told apart
-// (an older call would have to be 2^19 calls back), and the top bit keeps
-// every tag apart from never-written (zero) memory.  Statistics entries use
-// (1 << 31 | generation << 12 | sequence of the team) the same way.
+// bits of every 64-bit word; statistics entries carry (1 << 31 | generation
+// << 12 | sequence iteration mod 4096).  The generation is the call's, the
+// same for every team (a workspace reused with another shape puts other
+// teams' words at the same addresses: a generation per team could repeat
+// there), and the top bit keeps every tag apart from never-written (zero)
+// memory.  Tags alone cannot keep old words out: a slot that no sequence
+// writes for a while keeps its word, and sixteen sequences (or 2^19 calls)
+// later the same tag comes round again.  So both kinds of words sit in two
+// buffers per team, one per parity of the team's sequence iteration, and a
+// member clears its own words of a buffer when it starts the sequence that
+// uses it.  Nobody still reads them then: this member finished the previous
+// sequence, which needed every member's statistics of that sequence, which
+// each member published only after finishing the sequence before, the
+// buffer's last user.  A member reads another's walk records of sequence i
+// only after merging that member's statistics of i, published after its
+// clear, so a record it polls is cleared or of sequence i; a statistics entry
+// polled before its owner cleared it is of sequence i - 2 or of an earlier
+// call, which the tag tells apart.
 __device__ __forceinline__ uint32_t gen_tag(const TeamSync& s) {
     return 0x80000000u | (((uint32_t)(s.base >> kTagShift) & 0x7ffffu) << 12);
 }
@@ -930,7 +939,23 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             else if (tid == 0) s_srow[0] = 0;
             s_depth[tid] = tid == 0 ? 1 : 0;
         }
-        __syncthreads();  // the row table and the children masks are complete
+        {
+            // this member's words of the buffer this sequence uses (its
+            // statistics entries, then its walk records) are cleared before it
+            // writes any of them: the stores complete before the barrier below
+            const int R = GREEDY ? N : 2 * N;
+            const int nclr = 2 * R + (GREEDY ? 0 : N * kMassRec);
+            uint64_t* const sb = a.stats + ((size_t)team * 2 + (iter & 1)) * (size_t)2 * R * W;
+            uint64_t* const mb =
+                GREEDY ? nullptr
+                       : reinterpret_cast<uint64_t*>(a.mass + ((size_t)team * 2 + (iter & 1)) * N * W * kMassRec);
+            for (int i = tid; i < nclr; i += kThreads) {
+                if (i < 2 * R) st_dev(&sb[2 * ((size_t)(i >> 1) * W + w) + (i & 1)], 0ull);
+                else st_dev(&mb[((size_t)((i - 2 * R) / kMassRec) * W + w) * kMassRec + (i - 2 * R) % kMassRec], 0ull);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();  // the row table and the children masks are complete; the clears are done
         if (!GREEDY) {
             // the walk's links, published by the merge's barriers
             int t = tid;
@@ -1108,7 +1133,7 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
 
             // ---- the walk (identical on every member) ----
             const double inv_t64 = a.inv_t64;
-            double* massb = a.mass + (size_t)team * N * W * kMassRec;
+            double* massb = a.mass + ((size_t)team * 2 + (iter & 1)) * N * W * kMassRec;
             int u = 0, len = 0, pass = 0, nrej = 0;
             bool res_active = false;  // target at u: residual s_res / Z, else softmax(q_u / T)
             double Z = 1.0, wx_cur = 0.0;
@@ -1484,7 +1509,7 @@ int make_plan(int B, int N, int V, int greedy, AcceptPlan& pl) {
     pl.stats_off = off;
     off += round_up((size_t)nteams * 2 * 2 * (greedy ? N : 2 * N) * W * sizeof(uint64_t), 256);
     pl.mass_off = off;
-    if (!greedy) off += round_up((size_t)nteams * N * W * kMassRec * sizeof(double), 256);
+    if (!greedy) off += round_up((size_t)nteams * 2 * N * W * kMassRec * sizeof(double), 256);
     pl.total = off;
     return TV_OK;
 }
