@@ -425,6 +425,44 @@ def test_accept_invalid_trees_between_valid_ones(tv):
         _compare_walk((a[ok], n[ok], t[ok]), {k: np.asarray(v)[ok] for k, v in ref.items()}, greedy)
 
 
+def test_accept_generation_advances_for_teams_without_valid_trees(tv):
+    """Every team control line holds the same generation after each call, also
+    when some teams verified only invalid trees (they merge nothing); a call
+    of another shape on the same workspace is then exact."""
+    B, N, V = 16, 17, 20000
+    W, teams, _ = tv.accept_plan(B, N, V, False)
+    assert teams == B and W >= 2
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    w = Workload("gen", B=B, N=N, Hq=1, Hkv=1, D=128, L=1, V=V, sigma_q=3.0, sigma_n=1.0, temperatures=(1.0,),
+                 tree="random", max_depth=5, data_seed=23)
+    q, p, draft, parent_t = accept_inputs(w, device=dev())
+    par = _np(parent_t).copy()
+    bad = np.arange(1, B, 2)
+    par[bad, 5] = 7  # parent after the node: invalid, so every odd team has nothing to verify
+    tpar = torch.from_numpy(par).to(dev())
+    ws = torch.zeros(max(tv.accept_workspace_bytes(B, N, V, g) for g in (0, 1)), dtype=torch.uint8, device=dev())
+    gens = []
+    for greedy in (False, True, False):
+        a, _, _ = tv.spec_accept(q, None if greedy else p, draft, tpar, seed=2, temperature=1.0, greedy=greedy,
+                                 workspace=ws)
+        torch.cuda.synchronize()
+        assert (_np(a)[bad] == -1).all()
+        lines = _np(ws[: ncu * 16 * 8].view(torch.int64).view(ncu, 16)[:, 0])
+        assert (lines == lines[0]).all(), f"control lines disagree after a call: {sorted(set(lines.tolist()))}"
+        gens.append(int(lines[0]))
+    assert gens[0] < gens[1] < gens[2]
+    # another shape on the same workspace
+    w2 = CONFIGS["c3"]
+    q2, p2, d2, par2 = accept_inputs(w2, device=dev())
+    need = tv.accept_workspace_bytes(w2.B, w2.N, w2.V, False)
+    ws2 = ws if ws.numel() >= need else torch.cat([ws, torch.zeros(need - ws.numel(), dtype=torch.uint8,
+                                                                   device=dev())])
+    a, n, t = tv.spec_accept(q2, p2, d2, par2, seed=4, temperature=0.7, workspace=ws2)
+    torch.cuda.synchronize()
+    ref = oracle.spec_accept(_np(q2), _np(p2), _np(d2), _np(par2), seed=4, temperature=_t32(0.7))
+    _compare_walk((_np(a), _np(n), _np(t)), ref, False)
+
+
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_accept_full_config(tv, name):
     w = CONFIGS[name]

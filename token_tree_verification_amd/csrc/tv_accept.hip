@@ -1382,6 +1382,15 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
             __syncthreads();
         }  // sampling
     }
+    // A team whose every tree was invalid merged nothing and so never advanced
+    // its lines: it does now.  None of its members tags a word in this call,
+    // so it does not matter when the others read the line.
+    if (!gen_done) {
+        if (!have_base)
+            sync.base = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_base >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)s_base);
+        advance_generation(sync, w, gen_done);
+    }
 
     // ---- arrival: the last workgroup reports the teams whose waits ran out.
     // Each workgroup's accept_len stores are made by its thread 0 before this
