@@ -869,9 +869,11 @@ __global__ __launch_bounds__(kThreads) void spec_accept_kernel(const AccArgs a) 
     sync.limit = a.spin_limit;
     sync.base = 0;
     // this call's tags carry the generation after the workspace's last one
-    // (read from the team's own line, before this workgroup's arrival; the
-    // load overlaps the first tree load); the last workgroup to arrive stores
-    // it in every line for the next call
+    // (read from the team's own line; the load overlaps the first tree load).
+    // Member 0 of each team advances the team's lines once every member has
+    // read them (after its first merge, or at the end when the team verified
+    // only invalid trees); when a wait ran out, the last workgroup to arrive
+    // moves every line past this call
     if (tid == 0) s_base = (ld_dev(&sync.line[0]) + 1) << kTagShift;
     bool have_base = false, gen_done = false;
 
