@@ -239,7 +239,11 @@ int tv_spec_accept_plan(int B, int N, int V, int greedy, int* team_size, int* te
  * covers every plan of trees up to 64 nodes, and of larger trees with few
  * enough sequences (256-node trees in sampling mode with 256 sequences need
  * 8.1 MiB and are refused); the first
- * call on a device zeroes its control words with a small kernel on `stream`.
+ * call on a device puts the array's control words in order with a small
+ * kernel on `stream` (every team line set to the largest generation found,
+ * wait marks and the arrival word cleared): if that first call is captured
+ * into a HIP graph, the kernel runs on every replay and each replay still
+ * gets a new generation.
  * Shapes whose plan (tv_spec_accept_workspace) needs more return
  * TV_ERR_SCRATCH before anything is enqueued.  Every call on one GPU shares
  * that GPU's array: calls that overlap on one GPU (other streams, other

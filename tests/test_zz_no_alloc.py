@@ -88,3 +88,60 @@ def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
     got = _call(lib, "noalloc", q, None, draft, parent, 0, 1.0, 1)
     for a, b in zip(want, got):
         assert np.array_equal(a, b)
+
+
+_FIRST_CALL_CAPTURED = r'''
+import ctypes, sys
+import numpy as np
+import torch
+sys.path[:0] = [ROOT, ROOT + "/tests"]
+import token_tree_verification_amd as tv
+from workloads import CONFIGS, accept_inputs
+P = ctypes.c_void_p
+lib = tv.library()
+lib.tv_spec_accept_noalloc.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                       ctypes.c_float, ctypes.c_int, P, P, P, P]
+lib.tv_spec_accept_noalloc.restype = ctypes.c_int
+dev = torch.device("cuda:0")
+w = CONFIGS["c3"]
+s = torch.cuda.Stream(dev)
+with torch.cuda.stream(s):
+    batches = [accept_inputs(w, device=dev, seed=seed) for seed in (101, 102, 103)]
+    q, p, draft, parent = (t.clone() for t in batches[0])
+    outs = [torch.full((w.B,), -9, dtype=torch.int32, device=dev),
+            torch.full((w.B, w.N), -9, dtype=torch.int32, device=dev),
+            torch.full((w.B, w.N), -9, dtype=torch.int32, device=dev)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):  # the process's first call of the entry point
+        rc = lib.tv_spec_accept_noalloc(P(q.data_ptr()), P(p.data_ptr()), P(draft.data_ptr()), P(parent.data_ptr()),
+                                        None, w.B, w.N, w.V, 7, 0.7, 0, *(P(o.data_ptr()) for o in outs),
+                                        P(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, rc
+    for rep in range(6):
+        for dst, src in zip((q, p, draft, parent), batches[rep % 3]):
+            dst.copy_(src)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.cpu().numpy().copy() for o in outs]
+        a, n, t = tv.spec_accept(q, p, draft, parent, seed=7, temperature=0.7)
+        torch.cuda.synchronize()
+        for x, y in zip(got, (a, n, t)):
+            assert np.array_equal(x, y.cpu().numpy()), f"replay {rep} differs from the workspace call"
+print("first-call-captured ok")
+'''
+
+
+@pytest.mark.timeout(300)
+def test_noalloc_first_call_captured_in_a_graph():
+    """In a fresh process the first call of the entry point (which puts the
+    scratch's control words in order) is captured into a HIP graph; replays
+    with new inputs in the same buffers match the workspace call every time."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = f"ROOT = {root!r}\n" + _FIRST_CALL_CAPTURED
+    res = subprocess.run([sys.executable, "-u", "-c", code], capture_output=True, text=True, timeout=240)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-4000:]
+    assert "first-call-captured ok" in res.stdout

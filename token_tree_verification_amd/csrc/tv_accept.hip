@@ -1650,15 +1650,37 @@ namespace {
 constexpr size_t kScratchBytes = TV_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-__global__ void zero_fill_kernel(uint4* __restrict__ p, size_t n16) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = uint4{0u, 0u, 0u, 0u};
+// Puts the scratch's control words in the state a call leaves them in: every
+// team line holds the same generation (the largest one found, so that running
+// this again never moves a generation back), no wait marks, arrival word 0.
+// Safe to run between any two calls: when the first call on a device is
+// captured into a HIP graph, this runs before the accept kernel on every
+// replay, and the replays still see a new generation each (zeroing the lines
+// instead would give every replay the same one, and a replay could take the
+// previous replay's statistics entries for its own).  One workgroup of
+// kMaxTeams threads.
+__global__ __launch_bounds__(kMaxTeams) void scratch_init_kernel(uint64_t* __restrict__ ctrl, uint64_t* __restrict__ done) {
+    __shared__ uint64_t s_g[kMaxTeams / kWave];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    uint64_t g = ctrl[(size_t)t * kCtrlLine];
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(g, off);
+        g = o > g ? o : g;
+    }
+    if (lane == 0) s_g[wv] = g;
+    __syncthreads();
+    g = s_g[0];
+    for (int i = 1; i < kMaxTeams / kWave; ++i) g = s_g[i] > g ? s_g[i] : g;
+    ctrl[(size_t)t * kCtrlLine] = g;
+    ctrl[(size_t)t * kCtrlLine + 2] = 0ull;
+    if (t == 0) *done = 0ull;
 }
 
-// The scratch's device address on the current device, with its control lines
-// (team generations, wait marks, arrival word) zeroed once, on `stream`,
-// before first use.  Every other word the kernel reads carries a nonzero tag,
-// so never-written scratch is never taken for data.  nullptr on failure.
+// The scratch's device address on the current device, with its control words
+// (team generations, wait marks, arrival word) put in order once, on
+// `stream`, before first use.  Every other word the kernel reads carries a
+// nonzero tag and is cleared by its owner before use, so never-written
+// scratch is never taken for data.  nullptr on failure.
 char* device_scratch(hipStream_t stream) {
     static std::mutex mu;
     static char* ptr[64] = {nullptr};
@@ -1668,9 +1690,11 @@ char* device_scratch(hipStream_t stream) {
     if (ptr[dev] == nullptr) {
         void* p = nullptr;
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
-        const size_t ctrl = (size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t);
-        const size_t n16 = (round_up(ctrl, 256) + 256) / 16;  // control lines and the arrival word
-        hipLaunchKernelGGL(zero_fill_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint4*>(p), n16);
+        // the plan's layout: control lines at offset 0, the arrival word after them
+        char* base = static_cast<char*>(p);
+        const size_t done_off = round_up((size_t)kMaxTeams * kCtrlLine * sizeof(uint64_t), 256);
+        hipLaunchKernelGGL(scratch_init_kernel, dim3(1), dim3(kMaxTeams), 0, stream, reinterpret_cast<uint64_t*>(base),
+                           reinterpret_cast<uint64_t*>(base + done_off));
         if (hipGetLastError() != hipSuccess) return nullptr;
         ptr[dev] = static_cast<char*>(p);
     }
