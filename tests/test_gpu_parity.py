@@ -129,6 +129,8 @@ def test_attention_tiny_full_compare(tv, w):
     (1, 17, 16, 1, 128, "chain"),
     (1, 6, 4, 1, 16384, "chain"),  # 26 splits of 24 rows: merge rounds of 12, 12 and 2
     (1, 64, 4, 1, 8192, "random"),  # 256 rows, 5 splits: the wide kernel's many-split merge
+    (5, 33, 64, 64, 100, "random"),  # 320 row groups of <= 64 rows: two workgroups per CU, ragged key tail
+    (3, 20, 96, 32, 1000, "random"),  # 96 groups of 60 rows, three splits: two workgroups per CU, split merge
 ])
 def test_attention_shapes(tv, B, N, Hq, Hkv, L, tree):
     w = Workload("shape", B=B, N=N, Hq=Hq, Hkv=Hkv, D=128, L=L, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),
@@ -199,6 +201,7 @@ def test_attention_large_trees(tv, B, N, Hq, Hkv, L):
     (4, 6, 4, 1, 4096, [6, 2, 6, 1], [4096, 100, 0, 4095]),           # many splits, some empty
     (3, 64, 4, 1, 8192, [64, 30, 1], [8192, 63, 5000]),               # wide kernel, empty splits
     (3, 130, 2, 1, 1500, [130, 65, 64], [1500, 700, 0]),              # two ancestor words, ragged
+    (5, 40, 64, 64, 200, [40, 1, 33, 40, 12], [200, 0, 33, 199, 64]),  # two workgroups per CU, ragged
 ])
 def test_attention_ragged(tv, B, N, Hq, Hkv, L, nodes, lens):
     """Per-sequence node counts and cache lengths; padding rows of the output

@@ -86,26 +86,13 @@ struct AttnArgs {
 
 struct Plan {
     int variant;  // key groups x tile keys x stages x row blocks per wave x waves:
-                  // 4x32x2x1x4, 4x32x2x2x4, 2x64x2x2x4, 1x64x4x1x8
+                  // 4x32x2x1x4, 4x32x2x2x4, 2x64x2x2x4, 1x64x4x1x8, 2x32x2x1x4
     int kg, kt, nw, rows, R, row_tiles, nsplit, tiles_per_split, cache_tiles, tree_tiles;
 };
 
-Plan make_plan(int B, int N, int Hq, int Hkv, int L) {
-    Plan p;
-    const int G = Hq / Hkv;
-    p.R = G * N;
-    int rbw = 2;
-    p.nw = 4;
-    if (p.R <= 32) {
-        p.variant = 0; p.kg = 4; p.kt = 32; rbw = 1;
-    } else if (p.R <= 64) {
-        p.variant = 1; p.kg = 4; p.kt = 32;
-    } else if (p.R <= 128) {
-        p.variant = 2; p.kg = 2; p.kt = 64;
-    } else {
-        p.variant = 3; p.kg = 1; p.kt = 64; rbw = 1; p.nw = 8;
-    }
-    p.rows = (p.nw / p.kg) * 32 * rbw;
+// Row tiles, tiles and splits of a plan whose kernel shape (kg, kt, nw, rows)
+// is set.
+void plan_splits(Plan& p, int B, int N, int Hkv, int L) {
     p.row_tiles = (p.R + p.rows - 1) / p.rows;
     p.cache_tiles = (L + p.kt - 1) / p.kt;
     p.tree_tiles = (N + p.kt - 1) / p.kt;
@@ -130,6 +117,35 @@ Plan make_plan(int B, int N, int Hq, int Hkv, int L) {
         nsplit = (p.cache_tiles + tps - 1) / tps;
     }
     p.nsplit = nsplit;
+}
+
+Plan make_plan(int B, int N, int Hq, int Hkv, int L) {
+    Plan p;
+    const int G = Hq / Hkv;
+    p.R = G * N;
+    int rbw = 2;
+    p.nw = 4;
+    if (p.R <= 32) {
+        p.variant = 0; p.kg = 4; p.kt = 32; rbw = 1;
+    } else if (p.R <= 64) {
+        p.variant = 1; p.kg = 4; p.kt = 32;
+    } else if (p.R <= 128) {
+        p.variant = 2; p.kg = 2; p.kt = 64;
+    } else {
+        p.variant = 3; p.kg = 1; p.kt = 64; rbw = 1; p.nw = 8;
+    }
+    p.rows = (p.nw / p.kg) * 32 * rbw;
+    plan_splits(p, B, N, Hkv, L);
+    // Up to 64 rows and more workgroups than CUs: two key groups of two
+    // 32-row waves (67 KB of LDS instead of 128) let two workgroups share a CU,
+    // so the grid runs in about half as many rounds and each CU keeps twice
+    // the copies in flight (B = 16, 40 heads, 60 nodes, L = 2048: 640
+    // workgroups, 141-142 us against 154-155 us).
+    if (p.variant == 1 && (long)B * Hkv * p.row_tiles * p.nsplit > kTargetWorkgroups) {
+        p.variant = 4; p.kg = 2; p.kt = 32;
+        p.rows = (p.nw / p.kg) * 32;
+        plan_splits(p, B, N, Hkv, L);
+    }
     return p;
 }
 
@@ -1347,6 +1363,13 @@ extern "C" int tv_tree_attention_ex(const uint16_t* Q, const uint16_t* K_cache, 
                 hipLaunchKernelGGL((tree_attention_kernel<2, 64, 2, 2, 4, true>), dim3(a.nblocks), dim3(256), 0, st, a);
             else
                 hipLaunchKernelGGL((tree_attention_kernel<2, 64, 2, 2, 4, false>), dim3(a.nblocks), dim3(256), 0, st,
+                                   a);
+            break;
+        case 4:
+            if (nt)
+                hipLaunchKernelGGL((tree_attention_kernel<2, 32, 2, 1, 4, true>), dim3(a.nblocks), dim3(256), 0, st, a);
+            else
+                hipLaunchKernelGGL((tree_attention_kernel<2, 32, 2, 1, 4, false>), dim3(a.nblocks), dim3(256), 0, st,
                                    a);
             break;
         default:
