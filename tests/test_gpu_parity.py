@@ -131,6 +131,7 @@ def test_attention_tiny_full_compare(tv, w):
     (1, 64, 4, 1, 8192, "random"),  # 256 rows, 5 splits: the wide kernel's many-split merge
     (5, 33, 64, 64, 100, "random"),  # 320 row groups of <= 64 rows: two workgroups per CU, ragged key tail
     (3, 20, 96, 32, 1000, "random"),  # 96 groups of 60 rows, three splits: two workgroups per CU, split merge
+    (5, 40, 64, 64, 0, "random"),  # two workgroups per CU, empty caches: tree tiles only
 ])
 def test_attention_shapes(tv, B, N, Hq, Hkv, L, tree):
     w = Workload("shape", B=B, N=N, Hq=Hq, Hkv=Hkv, D=128, L=L, V=16, sigma_q=1, sigma_n=1, temperatures=(1.0,),
