@@ -9,10 +9,13 @@
 //
 // Design (gfx950):
 //  * The G = Hq/Hkv query heads sharing a KV head and the N tree nodes are
-//    packed into R = G*N query rows per (sequence, KV head).  A wave owns 64
-//    rows as two 32-row MFMA blocks; a workgroup's four waves form KG key
-//    groups of 4/KG row-waves, so one K/V byte read from HBM serves up to 256
-//    rows (grouped-query heads share it).
+//    packed into R = G*N query rows per (sequence, KV head).  A wave owns 32
+//    or 64 rows (one or two 32-row MFMA blocks); a workgroup's four waves form
+//    KG key groups of 4/KG row-waves (up to 64 rows on grids larger than the
+//    device: two key groups of two 32-row waves, small enough in LDS for two
+//    workgroups per CU), and the large-row kernel's eight waves own 256 rows,
+//    so one K/V byte read from HBM serves up to 256 rows (grouped-query heads
+//    share it).
 //  * K and V tiles go from HBM straight to LDS (global_load_lds, 16 bytes per
 //    lane) into an S-stage ring per key group, S - 1 tiles ahead of the
 //    arithmetic.  Rows of 256 bytes are stored with their 16-byte chunks
